@@ -1,0 +1,167 @@
+"""Pins for the oracle's group-shared scan (proxy + refine) and block-pooled coarse filter: hand
+cases for the proxy and the pooled keys, and the reductions in which each variant must give
+exactly the dense indexer's result."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+
+def _bits(x):
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+# -------------------------------------------------------------------------- proxy query
+
+def test_proxy_identical_members_is_member():
+    p = W.make_prefill(32, 4, 32, seed=1, rho=0.0)
+    p.q[0, 8:16] = p.q[0, 8]
+    # weights with few significant bits, so that their fp32 partial sums are exact
+    p.w[0, 8:16] = (np.round(p.w[0, 8] * 256) / 256).astype(np.float32)
+    qb, wb, pos = oracle.proxy_query(p, 0, 1, 8)
+    assert np.array_equal(qb, p.q[0, 8]) and np.array_equal(wb, p.w[0, 8]) and pos == 15
+
+
+def test_proxy_hand_mean():
+    # members 1, 2, 4 (bf16 exact): fp32 sum 7, 7/3 = 0x40155555 -> bf16 0x4015 (2.328125)
+    H, D = 1, 2
+    q = np.array([[1.0, -1.0], [2.0, 1.0], [4.0, 0.0]], np.float32).reshape(1, 3, H, D)
+    qb = W.f32_to_bf16_bits(q)
+    w = np.array([0.5, 0.25, 1.0], np.float32).reshape(1, 3, 1)
+    p = W.Problem(qb, W.BF16, W.f32_to_bf16_bits(np.zeros((1, 4, D), np.float32)), W.BF16, None,
+                  w, np.array([[1, 2, 3]], np.int32), np.array([4], np.int32))
+    pq, pw, pos = oracle.proxy_query(p, 0, 0, 4)
+    assert pq[0].tolist() == [0x4015, 0x0000]     # mean(-1, 1, 0) = 0
+    assert pw[0] == np.float32(np.float32(1.75) / np.float32(3.0))
+    assert pos == 3
+
+
+def test_proxy_opposite_members_cancel():
+    p = W.make_prefill(4, 2, 16, seed=2, q_dtype=W.F32, k_dtype=W.F32)
+    p.q[0, 1] = -p.q[0, 0]
+    qb, _, _ = oracle.proxy_query(p, 0, 0, 2)
+    assert (qb == 0).all()
+
+
+# -------------------------------------------------------------------------- group reductions
+
+@pytest.fixture(scope="module")
+def pre():
+    return W.make_prefill(160, 4, 32, seed=11, rho=0.9)
+
+
+def test_group_full_candidates_equals_dense(pre):
+    k = 24
+    d_idx, d_sc = oracle.dense(pre, k)
+    for G in (1, 5, 16):
+        g_idx, g_sc, _ = oracle.group(pre, k, G, pre.N)      # candidates = whole prefix
+        for t in range(pre.T):
+            assert set(g_idx[0, t].tolist()) == set(d_idx[0, t].tolist())
+        assert np.array_equal(np.sort(g_sc, -1), np.sort(d_sc, -1))
+
+
+def test_group_singletons_equal_dense(pre):
+    k = 24
+    d_idx, _ = oracle.dense(pre, k)
+    g_idx, _, _ = oracle.group(pre, k, 1, k)                # G=1: proxy == query, C = k
+    for t in range(pre.T):
+        assert set(g_idx[0, t].tolist()) == set(d_idx[0, t].tolist())
+
+
+def test_group_outputs_within_candidates(pre):
+    k, G, C = 16, 8, 40
+    g_idx, _, cands = oracle.group(pre, k, G, C)
+    for t in range(pre.T):
+        g = t // G
+        cand = cands[(0, g)]
+        gl = min(pre.T, (g + 1) * G) - 1
+        assert len(cand) == min(C, gl + 1)
+        sel = g_idx[0, t][g_idx[0, t] >= 0]
+        assert set(sel.tolist()) <= set(cand.tolist())
+        vis = cand[cand <= t]
+        assert len(sel) == min(k, len(vis))
+
+
+def test_group_partial_last_group():
+    p = W.make_prefill(37, 2, 16, seed=3)
+    _, _, cands = oracle.group(p, 8, 16, 20)
+    assert sorted(cands) == [(0, 0), (0, 1), (0, 2)]
+    qb, wb, pos = oracle.proxy_query(p, 0, 2, 16)             # members 32..36
+    assert pos == 36
+
+
+# -------------------------------------------------------------------------- block pooling
+
+def test_pool_hand_mean_partial_block():
+    # block size 3, k_len 5: blocks {1,2,3} -> 2 and {4,8} -> 6 (partial), per dim
+    k = np.array([[1, 0], [2, 0], [3, 3], [4, -1], [8, 1], [100, 100]], np.float32)[None]
+    p = W.Problem(np.zeros((1, 1, 1, 2), np.float32), W.F32, k, W.F32, None,
+                  np.ones((1, 1, 1), np.float32), np.array([[4]], np.int32),
+                  np.array([5], np.int32))
+    pk = oracle.pool_keys(p, 0, 3)
+    assert pk.tolist() == [[2.0, 1.0], [6.0, 0.0]]
+
+
+def test_pool_block_size_one_is_identity():
+    p = W.make_prefill(50, 2, 32, seed=4)
+    assert np.array_equal(oracle.pool_keys(p, 0, 1), p.k[0])
+
+
+def test_pool_constant_block():
+    p = W.make_prefill(64, 2, 32, seed=5)
+    p.k[0, 16:32] = p.k[0, 16]
+    pk = oracle.pool_keys(p, 0, 16)
+    assert np.array_equal(pk[1], p.k[0, 16])
+
+
+def test_block_hand_eligibility():
+    # D=1, H=1, w=1, q=1, block size 2, keys 0..5 = 1,1,5,5,9,9 ; pooled 1,5,9
+    k = np.array([1, 1, 5, 5, 9, 9], np.float32).reshape(1, 6, 1)
+    q = np.ones((1, 2, 1, 1), np.float32)
+    p = W.Problem(q, W.F32, k, W.F32, None, np.ones((1, 2, 1), np.float32),
+                  np.array([[2, 4]], np.int32), np.array([6], np.int32))
+    pooled = oracle.pool_keys(p, 0, 2)
+    inp = oracle.Inputs(p)
+    # pos 2: blocks 0 and 1 eligible (block 1 starts at 2); keep 1 -> block 1, token 3 is future
+    r = oracle.block_row(inp, 0, 0, 4, 2, 1, pooled)
+    assert r["blocks"].tolist() == [1] and r["ids"].tolist() == [2]
+    # pos 4: block 2 (start 4) eligible and best; only token 4 visible
+    r = oracle.block_row(inp, 0, 1, 4, 2, 1, pooled)
+    assert r["blocks"].tolist() == [2] and r["ids"].tolist() == [4]
+    r = oracle.block_row(inp, 0, 1, 2, 2, 2, pooled)
+    assert r["blocks"].tolist() == [1, 2] and r["ids"].tolist() == [4, 2]
+
+
+@pytest.fixture(scope="module")
+def hier():
+    return W.make_hier(512, 48, H=4, D=32, seed=7, n_regions=4, region=32)
+
+
+def test_block_keep_all_equals_dense(hier):
+    k = 40
+    d_idx, d_sc = oracle.dense(hier, k)
+    for bs in (7, 32):
+        b_idx, b_sc, _ = oracle.block(hier, k, bs, 10 ** 6)
+        for t in range(hier.T):
+            assert set(b_idx[0, t].tolist()) == set(d_idx[0, t].tolist())
+        assert np.array_equal(np.sort(b_sc, -1), np.sort(d_sc, -1))
+
+
+def test_block_size_one_keep_k_equals_dense(hier):
+    k = 40
+    d_idx, _ = oracle.dense(hier, k)
+    b_idx, _, _ = oracle.block(hier, k, 1, k)
+    for t in range(hier.T):
+        assert set(b_idx[0, t].tolist()) == set(d_idx[0, t].tolist())
+
+
+def test_block_outputs_within_kept_blocks(hier):
+    k, bs, keep = 64, 16, 6
+    b_idx, _, blks = oracle.block(hier, k, bs, keep)
+    for t in range(hier.T):
+        kept = blks[0, t][blks[0, t] >= 0]
+        assert len(kept) == min(keep, hier.q_pos[0, t] // bs + 1)
+        sel = b_idx[0, t][b_idx[0, t] >= 0]
+        assert set((sel // bs).tolist()) <= set(kept.tolist())
+        assert sel.max() <= hier.q_pos[0, t]
