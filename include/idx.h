@@ -1,0 +1,140 @@
+/* idx.h - C ABI of libidx.so, an MI355X (gfx950) implementation of the DeepSeek Sparse
+ * Attention lightning indexer and two of its published accelerations.
+ *
+ * The indexer scores, for every query t, each key s of its causal prefix with
+ *     I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . k[s])
+ * (H indexer heads, one shared indexer key per token, fp32 head weights) and keeps the k
+ * best-scoring tokens of each query. All five source pages build on this indexer ("ADIndex:
+ * Layer-Adaptive Sparse Attention Indexing via Group-Level Distillation", abstract; "Multi-layer
+ * Indexer ...", authors' abstract, k = 2048; "PIVOT: Efficient Query-Group Indexing for
+ * Token-Level Sparse Attention", abstract; "HISA: Efficient Hierarchical Indexing for
+ * Fine-Grained Sparse Attention", abstract; "LatentIndex: Cross-Layer Sharing with
+ * Layer-Specific Selection for Sparse Attention", abstract).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers (HIP device memory of the current device) unless stated.
+ *     `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
+ *     enqueues work on `stream` and returns; it never allocates, frees or synchronises.
+ *   - The caller owns all buffers. Scratch memory is the caller's `ws` buffer of `ws_bytes`
+ *     bytes, at least idx_workspace_bytes(...) for the same arguments.
+ *   - Output rows hold a SET of token indices: the first n = min(k, visible candidates) entries
+ *     are distinct token indices (within the sequence, 0..N-1) in ascending order, the rest are
+ *     -1; out_score (optional, may be NULL) holds the fp32 score of each index and -inf for the
+ *     padding. When several tokens tie with the k-th best score, the lowest indices are kept.
+ *   - Return value: IDX_OK or a negative IDX_ERR_* code. Argument errors are detected before
+ *     anything is enqueued. Device-array contents are preconditions and are not checked:
+ *     0 <= k_len[b] <= N, keys and queries finite, fp8 scales >= 0 and finite.
+ *   - Thread safety: calls are reentrant; calls that share a workspace on different streams race.
+ */
+#ifndef IDX_H_
+#define IDX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element formats */
+enum {
+  IDX_F32 = 0,       /* IEEE binary32 */
+  IDX_BF16 = 1,      /* bfloat16 (upper half of binary32) */
+  IDX_FP8_E4M3 = 2   /* OCP FP8 E4M3FN, one fp32 scale per token: key = decode(byte) * scale */
+};
+
+/* status codes */
+enum {
+  IDX_OK = 0,
+  IDX_ERR_INVALID_ARG = -1,  /* null required pointer, size <= 0, k <= 0, bad group/block args */
+  IDX_ERR_UNSUPPORTED = -2,  /* dtype / H / D / size combination not built (see below)        */
+  IDX_ERR_ALIGN = -3,        /* q, k or w not 16-byte aligned, or k_scale/q_pos/k_len not 4    */
+  IDX_ERR_WORKSPACE = -4,    /* ws NULL or ws_bytes < idx_workspace_bytes(...)                 */
+  IDX_ERR_HIP = -5,          /* a HIP launch reported an error                                  */
+  IDX_ERR_INTERNAL = -6      /* unexpected internal failure (no exception crosses the ABI)     */
+};
+
+/* operation ids for idx_workspace_bytes */
+enum { IDX_OP_SCORE_TOPK = 0, IDX_OP_GROUP = 1, IDX_OP_BLOCK = 2 };
+
+/* The indexer's inputs. Layouts are dense and row-major.
+ *   q       [B, T, H, D]  q_dtype IDX_F32 or IDX_BF16
+ *   k       [B, N, D]     k_dtype IDX_F32, IDX_BF16 or IDX_FP8_E4M3 (the per-layer key cache)
+ *   k_scale [B, N] fp32   required iff k_dtype == IDX_FP8_E4M3, else ignored
+ *   w       [B, T, H] fp32 head weights, any sign
+ *   q_pos   [B, T] int32  position of each query: key s is visible to query (b,t) iff
+ *                         s <= q_pos[b,t] and s < k_len[b] (the query's own token is visible);
+ *                         q_pos < 0 means an empty prefix
+ *   k_len   [B] int32     keys present in each sequence's cache, or NULL for N
+ * Built shapes: H in 1..128, D in {32, 64, 128}. Prefill (T large) and decode (T = 1..4 multi-token
+ * prediction queries against a long cache) use the same call. */
+typedef struct idx_problem {
+  int32_t B, T, H, D, N;
+  int32_t q_dtype, k_dtype;
+  const void* q;
+  const void* k;
+  const float* k_scale;
+  const float* w;
+  const int32_t* q_pos;
+  const int32_t* k_len;
+} idx_problem;
+
+/* Dense lightning indexer: score every visible key of every query and keep the top k.
+ *   out_idx   [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional).
+ * Source: the indexer itself ("Multi-layer Indexer ...", authors' abstract: every layer's indexer
+ * scores the whole cache and keeps the k = 2048 best tokens; "PIVOT ...", abstract: the scan over
+ * every preceding token costs O(L^2) per layer). */
+int idx_score_topk(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Group-shared scan with per-query refine ("PIVOT ...", abstract; PIVOT-Refine).
+ * Queries are cut into groups of `group_size` consecutive queries (the last group may be
+ * shorter). Each group is reduced to one proxy query: the element-wise mean of its queries and
+ * of their head weights (fp32 sum in ascending query order, one fp32 division, rounded to bf16
+ * nearest-even for bf16 queries), positioned at the largest member position. The proxy scores its
+ * prefix once and keeps its n_cand best tokens (the candidate set, min(n_cand, prefix) entries).
+ * Every member then scores the candidates inside its own prefix with its own query and weights
+ * and keeps its top k.
+ *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
+ *   out_cand [B, ceil(T/group_size), n_cand] int32 (optional): each group's candidates,
+ *            ascending, -1 padded.
+ * With n_cand >= the prefix length the result equals idx_score_topk's. Requires n_cand <= N. */
+int idx_group_proxy_refine(const idx_problem* p, int32_t k, int32_t group_size, int32_t n_cand,
+                           int32_t* out_idx, float* out_score, int32_t* out_cand,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Hierarchical block-coarse / token-refine indexer ("HISA ...", abstract).
+ * The key cache is cut into blocks of `block_size` consecutive tokens; each block present in the
+ * cache is pooled into one key (mean of its tokens: fp32 sum in ascending token order, one fp32
+ * division, rounded to bf16 nearest-even for bf16 keys). A query scores the pooled blocks whose
+ * first token is in its prefix (same score formula), keeps its n_blocks_keep best blocks, then
+ * scores the tokens of the kept blocks inside its prefix and keeps its top k.
+ *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
+ *   out_blocks [B, T, n_blocks_keep] int32 (optional): kept block ids, ascending, -1 padded.
+ * Keys must be IDX_BF16 or IDX_F32 (IDX_ERR_UNSUPPORTED for fp8). Requires
+ * ceil(N / block_size) <= 65536 and n_blocks_keep <= 32767. With n_blocks_keep >= the number of
+ * eligible blocks the result equals idx_score_topk's. */
+int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
+                            int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
+                            int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by one call. op = IDX_OP_*; p1, p2 = (group_size, n_cand) for
+ * IDX_OP_GROUP, (block_size, n_blocks_keep) for IDX_OP_BLOCK, ignored for IDX_OP_SCORE_TOPK.
+ * Only the shape fields of *p are read (pointers may be NULL). Returns 0 for invalid arguments. */
+size_t idx_workspace_bytes(int op, const idx_problem* p, int32_t k, int32_t p1, int32_t p2);
+
+/* Static, human-readable text for a status code. */
+const char* idx_strerror(int status);
+
+/* Kernel timing (host-side switch, for benchmarking). While enabled, every library call
+ * records a HIP event pair around each kernel launch on the call's stream. idx_timer_read
+ * waits for the recorded events, returns the summed milliseconds and the launch count of the
+ * kernels whose name contains `kernel_substr` (all kernels if NULL or ""), and clears the
+ * record. idx_timer_enable(0) disables recording and clears it. Not thread safe. */
+int idx_timer_enable(int on);
+int idx_timer_read(const char* kernel_substr, double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IDX_H_ */

@@ -1,0 +1,220 @@
+"""Python binding of libidx.so, the MI355X DeepSeek-Sparse-Attention lightning indexer.
+
+Argument marshalling only: every step of the indexer runs in the library's HIP kernels. Tensors
+must be on the GPU; the library is loaded from this package directory and its absence is an
+error (there is no other implementation to fall back to).
+
+    idx, score = score_topk(q, k, w, q_pos, topk=2048)
+    idx, score, cand = group_proxy_refine(q, k, w, q_pos, topk=2048, group_size=16, n_cand=8192)
+    idx, score, blocks = block_coarse_refine(q, k, w, q_pos, topk=2048, block_size=128,
+                                             n_blocks_keep=128)
+
+Shapes: q [B,T,H,D] (bf16 or fp32), k [B,N,D] (bf16, fp32, or float8_e4m3fn / uint8 E4M3FN
+bytes with k_scale [B,N] fp32), w [B,T,H] fp32, q_pos [B,T] int32, k_len [B] int32 or None.
+Outputs: int32 [B,T,topk] token indices (ascending, -1 padded) and fp32 scores (-inf padded).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["F32", "BF16", "FP8_E4M3", "IdxError", "lib", "score_topk", "group_proxy_refine",
+           "block_coarse_refine", "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+OP_SCORE_TOPK, OP_GROUP, OP_BLOCK = 0, 1, 2
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidx.so")
+EXPORTS = ["idx_score_topk", "idx_group_proxy_refine", "idx_block_coarse_refine",
+           "idx_workspace_bytes", "idx_strerror", "idx_timer_enable", "idx_timer_read"]
+
+
+class IdxError(RuntimeError):
+    pass
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("N", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+                ("k_dtype", ctypes.c_int32), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("w", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
+                ("k_len", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises IdxError if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise IdxError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_attention_indexer_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.idx_score_topk.argtypes = [P, i32, vp, vp, vp, sz, vp]
+        L.idx_group_proxy_refine.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.idx_block_coarse_refine.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.idx_workspace_bytes.argtypes = [ctypes.c_int, P, i32, i32, i32]
+        L.idx_workspace_bytes.restype = sz
+        L.idx_strerror.argtypes = [ctypes.c_int]
+        L.idx_strerror.restype = ctypes.c_char_p
+        L.idx_timer_enable.argtypes = [ctypes.c_int]
+        L.idx_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int32)]
+        for f in ("idx_score_topk", "idx_group_proxy_refine", "idx_block_coarse_refine",
+                  "idx_timer_enable", "idx_timer_read"):
+            getattr(L, f).restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise IdxError(f"{what}: {lib().idx_strerror(status).decode()} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise IdxError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise IdxError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _qcode(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise IdxError(f"unsupported query dtype {t.dtype}")
+
+
+def _kcode(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FP8_E4M3
+    raise IdxError(f"unsupported key dtype {t.dtype}")
+
+
+def make_problem(q, k, w, q_pos, k_len=None, k_scale=None) -> Problem:
+    """Fill the ABI's problem struct from tensors (shape checks only)."""
+    if q.dim() != 4 or k.dim() != 3 or w.dim() != 3 or q_pos.dim() != 2:
+        raise IdxError("expected q [B,T,H,D], k [B,N,D], w [B,T,H], q_pos [B,T]")
+    B, T, H, D = q.shape
+    N = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != D or tuple(w.shape) != (B, T, H) or \
+            tuple(q_pos.shape) != (B, T):
+        raise IdxError("inconsistent shapes")
+    if w.dtype != torch.float32 or q_pos.dtype != torch.int32:
+        raise IdxError("w must be float32 and q_pos int32")
+    if k_len is not None and (k_len.dtype != torch.int32 or tuple(k_len.shape) != (B,)):
+        raise IdxError("k_len must be int32 [B]")
+    kc = _kcode(k)
+    if kc == FP8_E4M3 and (k_scale is None or k_scale.dtype != torch.float32 or
+                           tuple(k_scale.shape) != (B, N)):
+        raise IdxError("fp8 keys need k_scale float32 [B,N]")
+    return Problem(B, T, H, D, N, _qcode(q), kc, _ptr(q), _ptr(k),
+                   _ptr(k_scale) if kc == FP8_E4M3 else None, _ptr(w), _ptr(q_pos), _ptr(k_len))
+
+
+def workspace_bytes(op: int, p: Problem, topk: int, p1: int = 0, p2: int = 0) -> int:
+    return int(lib().idx_workspace_bytes(op, ctypes.byref(p), topk, p1, p2))
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _outputs(q, topk, out_idx, out_score, want_score):
+    B, T = q.shape[:2]
+    if out_idx is None:
+        out_idx = torch.empty((B, T, topk), dtype=torch.int32, device=q.device)
+    if out_score is None and want_score:
+        out_score = torch.empty((B, T, topk), dtype=torch.float32, device=q.device)
+    return out_idx, out_score
+
+
+def _workspace(q, need, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < need:
+            raise IdxError("workspace too small")
+        return workspace
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+
+
+def score_topk(q, k, w, q_pos, topk: int = 2048, k_len=None, k_scale=None, out_idx=None,
+               out_score=None, want_score: bool = True, workspace=None, stream=None):
+    """Dense lightning indexer (idx_score_topk)."""
+    p = make_problem(q, k, w, q_pos, k_len, k_scale)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    need = workspace_bytes(OP_SCORE_TOPK, p, topk)
+    ws = _workspace(q, need, workspace)
+    _check(lib().idx_score_topk(ctypes.byref(p), topk, _ptr(out_idx), _ptr(out_score),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(q, stream)),
+           "idx_score_topk")
+    return out_idx, out_score
+
+
+def group_proxy_refine(q, k, w, q_pos, topk: int = 2048, group_size: int = 16,
+                       n_cand: int = 8192, k_len=None, k_scale=None, out_idx=None,
+                       out_score=None, want_score: bool = True, return_cand: bool = False,
+                       workspace=None, stream=None):
+    """Group-shared proxy scan + per-query refine (idx_group_proxy_refine)."""
+    p = make_problem(q, k, w, q_pos, k_len, k_scale)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    cand = None
+    if return_cand:
+        NG = (q.shape[1] + group_size - 1) // group_size
+        cand = torch.empty((q.shape[0], NG, n_cand), dtype=torch.int32, device=q.device)
+    need = workspace_bytes(OP_GROUP, p, topk, group_size, n_cand)
+    ws = _workspace(q, need, workspace)
+    _check(lib().idx_group_proxy_refine(ctypes.byref(p), topk, group_size, n_cand, _ptr(out_idx),
+                                        _ptr(out_score), _ptr(cand), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(q, stream)),
+           "idx_group_proxy_refine")
+    return out_idx, out_score, cand
+
+
+def block_coarse_refine(q, k, w, q_pos, topk: int = 2048, block_size: int = 128,
+                        n_blocks_keep: int = 128, k_len=None, out_idx=None, out_score=None,
+                        want_score: bool = True, return_blocks: bool = False, workspace=None,
+                        stream=None):
+    """Block-pooled coarse filter + token refine (idx_block_coarse_refine)."""
+    p = make_problem(q, k, w, q_pos, k_len, None)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    blocks = None
+    if return_blocks:
+        blocks = torch.empty((q.shape[0], q.shape[1], n_blocks_keep), dtype=torch.int32,
+                             device=q.device)
+    need = workspace_bytes(OP_BLOCK, p, topk, block_size, n_blocks_keep)
+    ws = _workspace(q, need, workspace)
+    _check(lib().idx_block_coarse_refine(ctypes.byref(p), topk, block_size, n_blocks_keep,
+                                         _ptr(out_idx), _ptr(out_score), _ptr(blocks), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(q, stream)),
+           "idx_block_coarse_refine")
+    return out_idx, out_score, blocks
+
+
+def timer_enable(on: bool = True):
+    _check(lib().idx_timer_enable(1 if on else 0), "idx_timer_enable")
+
+
+def timer_read(kernel_substr: str = ""):
+    """(total milliseconds, launches) of the recorded kernels whose name contains the text."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int32(0)
+    _check(lib().idx_timer_read(kernel_substr.encode(), ctypes.byref(ms), ctypes.byref(n)),
+           "idx_timer_read")
+    return ms.value, n.value

@@ -1,0 +1,147 @@
+// Device-side building blocks shared by the indexer kernels (gfx950 / CDNA4).
+//
+// Score contraction: for one query t and a block of 32 keys, the head dot products
+// x[h, n] = q[t,h,:] . k[n,:] are one 32x32 MFMA tile per group of 32 heads (rows = heads,
+// columns = keys), accumulated in fp32 over D. The fused epilogue reduces the tile to one score
+// per key, I[t,n] = sum_h w[t,h] * max(x[h,n], 0), in registers: each lane holds 16 heads of one
+// key per tile, lanes l and l+32 hold complementary heads, one cross-lane add finishes the sum.
+// (DeepSeek Sparse Attention's lightning-indexer score; the five indexer pages build on it.)
+//
+// Operand layout: lane l works on key/head row (l % 32) and on HALF of the head dimension,
+// hh = l / 32 covers d in [hh*D/2, (hh+1)*D/2). Step kk of the contraction consumes E
+// consecutive elements of that half (E = 8 for bf16 32x32x16, E = 1 for fp32 32x32x2). The same
+// permutation of d is applied to queries and keys, so the dot products are unchanged.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+// ---------------------------------------------------------------------------------------------
+// number formats
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// OCP FP8 E4M3FN byte -> bf16 bits, exact (every E4M3 value is a bf16 value). Normal codes:
+// exponent rebias 7 -> 127 and mantissa moved to the top of bf16's 7 bits. Subnormal codes
+// m * 2^-9 are normalised by a 3-entry shift. The NaN code (S.1111.111) maps to a bf16 NaN.
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t b) {
+  uint32_t s = (b & 0x80u) << 8;
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  uint32_t mag;
+  if (e != 0) {
+    mag = ((e + 120u) << 7) | (m << 4);
+    if (e == 15u && m == 7u) mag = 0x7FC0u;
+  } else if (m == 0) {
+    mag = 0;
+  } else {
+    // m in 1..7: value m*2^-9; leading bit position p = floor(log2 m)
+    uint32_t p = 31u - __builtin_clz(m);
+    uint32_t frac = (m << (7u - p)) & 0x7Fu;        // bits below the leading one, left-aligned
+    mag = ((118u + p) << 7) | frac;                 // 2^-9 * 2^p -> biased exponent 118 + p
+  }
+  return s | mag;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __uint_as_float(e4m3_to_bf16_bits(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even, NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Order-preserving map float -> uint32 (larger float <=> larger key). 0 is below every
+// non-NaN float (-inf maps to 0x007FFFFF) and marks "no score" slots.
+__device__ __forceinline__ uint32_t f2key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+constexpr uint32_t KEY_NONE = 0u;
+
+// ---------------------------------------------------------------------------------------------
+// MFMA flavours. Elements live in LDS in the flavour's element type.
+
+struct MmaBf16 {
+  static constexpr int kElemBytes = 2;
+  static constexpr int E = 8;                  // elements per lane per instruction
+  typedef bf16x8_t frag_t;
+  static __device__ __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct MmaF32 {
+  static constexpr int kElemBytes = 4;
+  static constexpr int E = 1;
+  typedef float frag_t;
+  static __device__ __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Head held by accumulator register r of lane l in head block hb (32x32 MFMA C layout:
+// row = 8*(r/4) + 4*(l/32) + r%4, column = l%32).
+__device__ __forceinline__ int acc_head(int hb, int r, int lane) {
+  return 32 * hb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// Load E elements of a query/key row, converting from its storage format into the MFMA
+// element type. `row` points at the row start, `e0` is the first element.
+template <class Mma>
+__device__ __forceinline__ typename Mma::frag_t load_frag(const void* row, int dtype, int e0);
+
+template <>
+__device__ __forceinline__ bf16x8_t load_frag<MmaBf16>(const void* row, int dtype, int e0) {
+  // only bf16 storage reaches here (queries of the bf16 path)
+  u32x4_t v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(row) + e0);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <>
+__device__ __forceinline__ float load_frag<MmaF32>(const void* row, int dtype, int e0) {
+  if (dtype == DT_F32) return reinterpret_cast<const float*>(row)[e0];
+  if (dtype == DT_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[e0]);
+  return e4m3_to_f32(reinterpret_cast<const uint8_t*>(row)[e0]);
+}
+
+// Bytes per element of a storage dtype.
+__host__ __device__ __forceinline__ int dtype_bytes(int dt) {
+  return dt == DT_F32 ? 4 : (dt == DT_BF16 ? 2 : 1);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wave-level helpers (wave64)
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T u = __shfl_up(v, o, 64);
+    if (l >= o) v += u;
+  }
+  return v;
+}
+
+}  // namespace idx

@@ -1,0 +1,86 @@
+// Internal kernel argument blocks and launchers (host side of the library only; not part of
+// the public C ABI in include/idx.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+
+// Score a tile of queries against a key set and write one fp32 score per (query, slot).
+//   RANGE mode: slot j is key j of the sequence's key array, visible to query t iff
+//               j * pos_stride <= q_pos[t] and j < ceil(k_len / count_div). Used by the dense
+//               indexer (pos_stride = count_div = 1) and by the pooled-block coarse scan
+//               (pos_stride = count_div = block size; key j = pooled block j).
+//   LIST  mode: slot j is key list[g][j] for the query's group g = t / group_size; a slot whose
+//               key is beyond q_pos[t] gets -inf. Used by the group refine.
+enum { MODE_RANGE = 0, MODE_LIST = 1 };
+
+struct ScoreArgs {
+  const void* q; int q_dtype;      // [B, T, H, D]
+  const float* w;                  // [B, T, H]
+  const int32_t* q_pos;            // [B, T]
+  const void* keys; int k_dtype;   // [B, key_cap, D]
+  const float* k_scale;            // [B, key_cap] (fp8 keys) or null
+  const int32_t* k_len;            // [B] tokens in the cache, or null (= tok_cap)
+  int B, T, H, D;
+  int key_cap;                     // key rows per sequence in `keys`
+  int tok_cap;                     // token capacity per sequence (N), for a null k_len
+  int mode, pos_stride, count_div;
+  const int32_t* list; const int32_t* list_len; int list_stride; int group_size; int n_groups;
+  int c0, c1;                      // RANGE: query range [c0,c1); LIST: group range [c0,c1)
+  float* scores; int64_t score_stride;
+  int32_t* row_len;                // slots per row, written by split 0
+  int rows_per_seq;                // score rows per sequence in this chunk
+  int tiles_per_seq;
+  int split_keys;                  // keys per grid.y split (multiple of the key tile)
+};
+
+// Pick rows from per-row score arrays: the top-k slots of each row, written in ascending slot
+// order (= ascending token order for every slot map used here).
+enum { MAP_IDENT = 0, MAP_LIST = 1, MAP_BLOCKS = 2 };
+
+struct TopkArgs {
+  const float* scores; int64_t score_stride;
+  const int32_t* row_len;
+  int n_rows, k;
+  int rows_per_seq, T_out, t_off;  // output row = (r / rows_per_seq) * T_out + t_off + r % rows_per_seq
+  int32_t* out_idx; float* out_score; int out_stride;
+  int32_t* out_count;              // optional: selections per output row
+  int map_mode;
+  const int32_t* list; int list_stride; int group_size; int n_groups;
+  const int32_t* blocks; int blocks_stride; int block_size;
+};
+
+struct ProxyArgs {
+  const void* q; int q_dtype; const float* w; const int32_t* q_pos;
+  int B, T, H, D, G, n_groups;
+  void* pq; float* pw; int32_t* ppos;   // [B, NG, H, D], [B, NG, H], [B, NG]
+};
+
+struct PoolArgs {
+  const void* keys; int k_dtype; const int32_t* k_len;
+  int B, N, D, block_size, n_blocks;    // n_blocks = ceil(N / block_size) (row capacity)
+  void* pooled;                          // [B, n_blocks, D] in the key format
+};
+
+struct BlockRefineArgs {
+  const void* q; int q_dtype; const float* w; const int32_t* q_pos;
+  const void* keys; int k_dtype; const int32_t* k_len;
+  int B, T, H, D, N;
+  const int32_t* blocks; const int32_t* n_kept; int keep_stride; int block_size;
+  int t0, t1;                            // query range of this chunk
+  float* scores; int64_t score_stride;   // slot = kept position * block_size + offset
+  int32_t* row_len; int rows_per_seq; int tiles_per_seq;
+};
+
+hipError_t launch_score(const ScoreArgs& a, int n_splits, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s);
+hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+hipError_t launch_block_refine(const BlockRefineArgs& a, hipStream_t s);
+bool score_supported(int q_dtype, int k_dtype, int H, int D);
+
+constexpr int KEY_TILE = 64;       // keys per LDS tile of the score kernels
+constexpr int Q_TILE = 8;          // queries per work-group tile (one per wave)
+
+}  // namespace idx
