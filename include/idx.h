@@ -128,9 +128,10 @@ const char* idx_strerror(int status);
 
 /* Kernel timing (host-side switch, for benchmarking). While enabled, every library call
  * records a HIP event pair around each kernel launch on the call's stream. idx_timer_read
- * waits for the recorded events, returns the summed milliseconds and the launch count of the
- * kernels whose name contains `kernel_substr` (all kernels if NULL or ""), and clears the
- * record. idx_timer_enable(0) disables recording and clears it. Not thread safe. */
+ * waits for the recorded events and returns the summed milliseconds and the launch count of
+ * the kernels whose name contains `kernel_substr` (all kernels if NULL or ""); kernel names are
+ * "score", "topk", "proxy", "pool" and "block_refine". idx_timer_enable(on) clears the record
+ * and switches recording on or off. Not thread safe. */
 int idx_timer_enable(int on);
 int idx_timer_read(const char* kernel_substr, double* total_ms, int32_t* launches);
 

@@ -463,11 +463,6 @@ int idx_timer_read(const char* kernel_substr, double* total_ms, int32_t* launche
       tot += ms;
       ++n;
     }
-    for (auto& r : g_recs) {
-      g_event_pool.push_back(r.a);
-      g_event_pool.push_back(r.b);
-    }
-    g_recs.clear();
     if (total_ms) *total_ms = tot;
     if (launches) *launches = n;
     return st;
