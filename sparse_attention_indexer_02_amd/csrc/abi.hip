@@ -16,7 +16,7 @@ int score_queries_per_tile(int H);
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kScoreBudget = size_t(256) << 20;   // score rows held per chunk (bytes)
+constexpr size_t kScoreBudget = size_t(1) << 30;     // score rows held per chunk (bytes)
 constexpr int kTargetGroups = 1024;                  // work-groups wanted per score launch
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

@@ -21,8 +21,8 @@ __global__ void __launch_bounds__(WavesFor<HB>::value * 64)
 block_refine_kernel(BlockRefineArgs a) {
   constexpr int NW = WavesFor<HB>::value;
   constexpr int NTHR = NW * 64;
-  typedef Geo<Mma, D> G;
-  typedef TileLoader<Mma, D, KST, NTHR> Loader;
+  typedef Geo<Mma, D, KEY_TILE> G;
+  typedef TileLoader<Mma, D, KST, NTHR, KEY_TILE> Loader;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tiles = smem;
   int16_t* pos_tab = reinterpret_cast<int16_t*>(smem + 2 * G::TILE_BYTES);   // [NW][UMAX]
@@ -166,7 +166,7 @@ block_refine_kernel(BlockRefineArgs a) {
         const int mem = (lane < 32 && v < nslots) ? pos_tab[wave * BR_UMAX + u] : -1;
         if (active && __ballot(mem >= 0) != 0ull) {
           f32x16_t acc[HB];
-          tile_mma<Mma, D, HB>(qf, tiles + cur * G::TILE_BYTES, sub * 32, lane, acc);
+          tile_mma<Mma, D, HB, KEY_TILE>(qf, tiles + cur * G::TILE_BYTES, sub * 32, lane, acc);
           const float tot = tile_epilogue<HB>(acc, wv);
           if (mem >= 0) {
             const int key = ublk[u] * Bs + o;
@@ -183,7 +183,7 @@ block_refine_kernel(BlockRefineArgs a) {
 template <class Mma, int D, int HB, int KST>
 static hipError_t launch_br(const BlockRefineArgs& a, hipStream_t s) {
   constexpr int NW = WavesFor<HB>::value;
-  typedef Geo<Mma, D> G;
+  typedef Geo<Mma, D, KEY_TILE> G;
   const size_t lds = 2 * G::TILE_BYTES + NW * BR_UMAX * sizeof(int16_t) +
                      BR_UMAX * sizeof(int32_t) + 2 * BR_NBW * sizeof(uint32_t) + 80 * sizeof(uint32_t);
   auto kfn = block_refine_kernel<Mma, D, HB, KST>;

@@ -16,26 +16,37 @@
 
 namespace idx {
 
-template <class Mma, int D, int HB, int KST>
+template <class Mma, int KST> struct Direct {
+  static constexpr bool value = sizeof(Mma) > 0 && Mma::E == 8 && KST == DT_BF16;
+};
+template <class Mma, int KST> struct TileKeys {
+  static constexpr int value = Direct<Mma, KST>::value ? 128 : 64;
+};
+
+template <class Mma, int D, int HB, int KST, bool LISTM>
 __global__ void __launch_bounds__(WavesFor<HB>::value * 64)
 score_kernel(ScoreArgs a) {
   constexpr int NW = WavesFor<HB>::value;
   constexpr int NTHR = NW * 64;
-  typedef Geo<Mma, D> G;
-  typedef TileLoader<Mma, D, KST, NTHR> Loader;
+  constexpr bool DIRECT = Direct<Mma, KST>::value;
+  constexpr int KT = TileKeys<Mma, KST>::value;
+  constexpr int NSUB = KT / 32;
+  constexpr bool META = LISTM || KST == DT_FP8;
+  typedef Geo<Mma, D, KT> G;
+  typedef TileLoader<Mma, D, KST, NTHR, KT> Loader;
+  typedef DirectLoader<D, NTHR, KT> DLoader;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tiles = smem;
-  int32_t* skey = reinterpret_cast<int32_t*>(smem + 2 * G::TILE_BYTES);   // [2][KEY_TILE]
-  float* sscale = reinterpret_cast<float*>(skey + 2 * KEY_TILE);           // [2][KEY_TILE]
+  int32_t* skey = reinterpret_cast<int32_t*>(smem + 2 * G::TILE_BYTES);   // [2][KT]
+  float* sscale = reinterpret_cast<float*>(skey + 2 * KT);                 // [2][KT]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lin = gridDim.x - 1 - blockIdx.x;       // heaviest tiles first
   const int b = lin % a.B;
   const int ti = lin / a.B;
-  const bool list_mode = a.mode == MODE_LIST;
 
   int tb, te, lrow = 0, row0;
-  if (!list_mode) {
+  if constexpr (!LISTM) {
     tb = a.c0 + ti * NW;
     te = min(tb + NW, a.c1);
     row0 = a.c0;
@@ -58,7 +69,7 @@ score_kernel(ScoreArgs a) {
   const bool active = t < te;
   const int my_pos = active ? a.q_pos[(int64_t)b * a.T + t] : -1;
   int my_count, key_end;
-  if (!list_mode) {
+  if constexpr (!LISTM) {
     my_count = active ? count_of(my_pos) : 0;
     key_end = 0;
     for (int u = tb; u < te; ++u) key_end = max(key_end, count_of(a.q_pos[(int64_t)b * a.T + u]));
@@ -72,6 +83,7 @@ score_kernel(ScoreArgs a) {
   const int kb0 = blockIdx.y * a.split_keys;
   const int kb1 = min(key_end, kb0 + a.split_keys);
   if (kb0 >= kb1) return;                           // uniform over the work-group
+  const int lim = min(my_count, kb1);               // this wave's last slot (exclusive)
 
   // query fragments and head weights of this wave's query
   typename Mma::frag_t qf[HB][G::NKK];
@@ -100,68 +112,142 @@ score_kernel(ScoreArgs a) {
 
   const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.keys) +
                         (int64_t)b * a.key_cap * (D * Loader::SRC_EB);
-  auto key_at = [&](int base, int n) -> int {
+  const int32_t* lst = LISTM ? a.list + (int64_t)lrow * a.list_stride : nullptr;
+  auto key_at = [&](int base, int n) -> int {       // key index of slot base + n, or -1
     const int j = base + n;
     if (j >= kb1) return -1;
-    return list_mode ? a.list[(int64_t)lrow * a.list_stride + j] : j;
+    if constexpr (LISTM) return lst[j];
+    else return j;
   };
   auto scale_of = [&](int ki) -> float {
     if constexpr (KST == DT_FP8) return ki >= 0 ? a.k_scale[(int64_t)b * a.key_cap + ki] : 0.f;
     else return 1.f;
   };
 
+  const int ntile = (kb1 - kb0 + KT - 1) / KT;
   Loader ld;
-  const int ntile = (kb1 - kb0 + KEY_TILE - 1) / KEY_TILE;
-  ld.load(kseq, tid, [&](int n) { return key_at(kb0, n); });
-  if (tid < KEY_TILE) {
-    const int ki = key_at(kb0, tid);
-    skey[tid] = ki;
-    sscale[tid] = scale_of(ki);
+  // direct path: key indices of the rows this thread's DMA chunks fill, one tile ahead
+  int kidx[DIRECT ? DLoader::ITERS : 1];
+  auto fetch_idx = [&](int base) {
+    if constexpr (DIRECT) {
+#pragma unroll
+      for (int i = 0; i < DLoader::ITERS; ++i) kidx[i] = key_at(base, DLoader::row_of(i, wave, lane));
+    }
+  };
+  auto issue_tile = [&](int buf, int base) {        // start filling LDS buffer `buf`
+    if constexpr (DIRECT) {
+      DLoader::load_idx(kseq, tiles + buf * G::TILE_BYTES, wave, lane, kidx);
+      if constexpr (LISTM) {
+#pragma unroll
+        for (int i = 0; i < DLoader::ITERS; ++i)
+          if (DLoader::first_chunk(i, wave, lane)) skey[buf * KT + DLoader::row_of(i, wave, lane)] = kidx[i];
+      }
+    } else {
+      ld.load(kseq, tid, [&](int n) { return key_at(base, n); });
+      if (META && tid < KT) {
+        const int ki = key_at(base, tid);
+        skey[buf * KT + tid] = ki;
+        sscale[buf * KT + tid] = scale_of(ki);
+      }
+    }
+  };
+
+  fetch_idx(kb0);
+  issue_tile(0, kb0);
+  if constexpr (DIRECT) {
+    if (ntile > 1) fetch_idx(kb0 + KT);
+    wait_vmem();
+  } else {
+    ld.store(tiles, tid);
   }
-  ld.store(tiles, tid);
   __syncthreads();
 
   float* srow = a.scores + ((int64_t)b * a.rows_per_seq + (active ? t - row0 : 0)) * a.score_stride;
+  bf16x8_t bfr[DIRECT ? G::NKK : 1];                 // rotating key fragments (bf16 path)
 
   for (int it = 0; it < ntile; ++it) {
     const int cur = it & 1;
-    const int base = kb0 + it * KEY_TILE;
+    const int base = kb0 + it * KT;
     const bool more = it + 1 < ntile;
-    int nki = -1;
-    float nsc = 0.f;
     if (more) {
-      ld.load(kseq, tid, [&](int n) { return key_at(base + KEY_TILE, n); });
-      if (tid < KEY_TILE) {
-        nki = key_at(base + KEY_TILE, tid);
-        nsc = scale_of(nki);
+      issue_tile(cur ^ 1, base + KT);
+      if constexpr (DIRECT) {
+        if (it + 2 < ntile) fetch_idx(base + 2 * KT);
       }
     }
-    if (active && base < my_count) {
-      const uint8_t* tile = tiles + cur * G::TILE_BYTES;
+    const uint8_t* tile = tiles + cur * G::TILE_BYTES;
+    // scores of this tile, two 32-key steps per value (lanes 0-31: even step, 32-63: odd step),
+    // kept in registers and stored after the wait for the next tile's loads, so that the wait
+    // never waits on this tile's stores
+    float ov[NSUB / 2];
 #pragma unroll
-      for (int sub = 0; sub < KEY_TILE / 32; ++sub) {
-        const int sbase = base + sub * 32;
-        if (sbase >= my_count || sbase >= kb1) break;
-        f32x16_t acc[HB];
-        tile_mma<Mma, D, HB>(qf, tile, sub * 32, lane, acc);
-        const float tot = tile_epilogue<HB>(acc, wv);
-        if (lane < 32) {
-          const int j = sbase + lane;
-          const int n = sub * 32 + lane;
-          if (j < kb1 && j < my_count) {
-            float v = tot;
-            if constexpr (KST == DT_FP8) v *= sscale[cur * KEY_TILE + n];
-            if (list_mode && skey[cur * KEY_TILE + n] > my_pos) v = -INFINITY;
-            srow[j] = v;
+    for (int p = 0; p < NSUB / 2; ++p) ov[p] = 0.f;
+    if (active && base + KT <= lim) {
+      // full tile: the epilogue of each 32-key step overlaps the MFMAs of the next one, and
+      // the next step's key fragments are read from LDS while this step's MFMAs run
+      f32x16_t A[HB], Bq[HB];
+      float t_prev = 0.f;
+      auto mma_step = [&](int s, f32x16_t (&acc)[HB]) {
+        if constexpr (DIRECT) {
+          tile_mma_rot<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, lane, acc);
+        } else {
+          tile_mma<Mma, D, HB, KT>(qf, tile, s * 32, lane, acc);
+        }
+      };
+      if constexpr (DIRECT) load_bfrag<D, KT>(tile, 0, lane, bfr);
+      mma_step(0, A);
+#pragma unroll
+      for (int s = 1; s < NSUB; ++s) {
+        float tcur;
+        if constexpr (DIRECT) __builtin_amdgcn_sched_barrier(0);
+        if (s & 1) {
+          mma_step(s, Bq);
+          tcur = tile_epilogue<HB>(A, wv);
+        } else {
+          mma_step(s, A);
+          tcur = tile_epilogue<HB>(Bq, wv);
+        }
+        if constexpr (DIRECT) {
+          // per key-fragment step: HB MFMAs, one LDS read of the next step, then a slice of
+          // the previous step's epilogue
+#pragma unroll
+          for (int kk = 0; kk < G::NKK; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, HB, 0);
+            if (s + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (16 * HB * 2 + 8) / G::NKK + 1, 0);
           }
         }
+        if ((s - 1) & 1) ov[(s - 2) / 2] = lane < 32 ? t_prev : tcur;
+        else t_prev = tcur;
+      }
+      const float tl = tile_epilogue<HB>(Bq, wv);
+      ov[NSUB / 2 - 1] = lane < 32 ? t_prev : tl;
+    } else if (active && base < lim) {
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        if (base + s * 32 >= lim) break;
+        f32x16_t A[HB];
+        tile_mma<Mma, D, HB, KT>(qf, tile, s * 32, lane, A);
+        const float tot = tile_epilogue<HB>(A, wv);
+        if ((s & 1) == (lane >> 5)) ov[s / 2] = tot;
       }
     }
     if (more) {
-      ld.store(tiles + (cur ^ 1) * G::TILE_BYTES, tid);
-      if (tid < KEY_TILE) {
-        skey[(cur ^ 1) * KEY_TILE + tid] = nki;
-        sscale[(cur ^ 1) * KEY_TILE + tid] = nsc;
+      if constexpr (DIRECT) wait_vmem();
+      else ld.store(tiles + (cur ^ 1) * G::TILE_BYTES, tid);
+    }
+    if (active) {
+#pragma unroll
+      for (int p = 0; p < NSUB / 2; ++p) {
+        const int n = p * 64 + lane;
+        if (base + n < lim) {
+          float v = ov[p];
+          if constexpr (KST == DT_FP8) v *= sscale[cur * KT + n];
+          if constexpr (LISTM) {
+            if (skey[cur * KT + n] > my_pos) v = -INFINITY;
+          }
+          srow[base + n] = v;
+        }
       }
     }
     __syncthreads();
@@ -182,9 +268,11 @@ bool score_supported(int q_dtype, int k_dtype, int H, int D) {
 template <class Mma, int D, int HB, int KST>
 static hipError_t launch_one(const ScoreArgs& a, int n_splits, hipStream_t s) {
   constexpr int NW = WavesFor<HB>::value;
-  typedef Geo<Mma, D> G;
-  const size_t lds = 2 * G::TILE_BYTES + 4 * KEY_TILE * sizeof(int32_t);
-  auto kfn = score_kernel<Mma, D, HB, KST>;
+  constexpr int KT = TileKeys<Mma, KST>::value;
+  typedef Geo<Mma, D, KT> G;
+  const size_t lds = 2 * G::TILE_BYTES + 4 * KT * sizeof(int32_t);
+  auto kfn = a.mode == MODE_LIST ? score_kernel<Mma, D, HB, KST, true>
+                                 : score_kernel<Mma, D, HB, KST, false>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

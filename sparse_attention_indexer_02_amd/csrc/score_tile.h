@@ -5,26 +5,33 @@
 
 namespace idx {
 
-template <class Mma, int D>
+template <class Mma, int D, int KT>
 struct Geo {
   static constexpr int EB = Mma::kElemBytes;
   static constexpr int ROW_BYTES = D * EB;
   static constexpr int CPR = ROW_BYTES / 16;          // 16-byte chunks per key row
   static constexpr int EPC = 16 / EB;                 // elements per chunk
-  static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;
-  static constexpr int TILE_BYTES = KEY_TILE * ROW_BYTES;
+  static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+  static constexpr int TILE_BYTES = KT * ROW_BYTES;
   static constexpr int NKK = D / 2 / Mma::E;          // MFMA steps per 32x32 tile
 };
 
 template <int HB> struct WavesFor { static constexpr int value = (HB <= 2) ? 8 : 4; };
 
-// Stages one tile of KEY_TILE keys from global memory (any key storage format) into LDS in the
-// MFMA element format. Global loads are issued early (load) and written to LDS later (store)
-// so that their latency overlaps the current tile's MFMA work.
-template <class Mma, int D, int KST, int NTHR>
+// Byte offset inside a tile of logical 16-byte chunk c of key row n (XOR swizzle: the 32 rows a
+// wave reads in one step start in different banks).
+template <class G>
+__device__ __forceinline__ int chunk_off(int n, int c) {
+  return n * G::ROW_BYTES + ((c ^ (n & G::SWZ)) << 4);
+}
+
+// Stages one tile of KT keys from global memory (any key storage format) into LDS in the MFMA
+// element format, through registers. Global loads are issued early (load) and written to LDS
+// later (store) so that their latency overlaps the current tile's MFMA work.
+template <class Mma, int D, int KST, int NTHR, int KT>
 struct TileLoader {
-  typedef Geo<Mma, D> G;
-  static constexpr int NCH = KEY_TILE * G::CPR;
+  typedef Geo<Mma, D, KT> G;
+  static constexpr int NCH = KT * G::CPR;
   static constexpr int ITERS = (NCH + NTHR - 1) / NTHR;
   static constexpr int SRC_EB = (KST == DT_F32 ? 4 : (KST == DT_BF16 ? 2 : 1));
   static constexpr int SRC_BYTES = G::EPC * SRC_EB;
@@ -91,39 +98,88 @@ struct TileLoader {
       const int cid = tid + i * NTHR;
       if (NCH % NTHR == 0 || cid < NCH) {
         const int n = cid / G::CPR, c = cid % G::CPR;
-        const int phys = c ^ (n & G::SWZ);
-        *reinterpret_cast<u32x4_t*>(tile + n * G::ROW_BYTES + phys * 16) = convert(raw[i]);
+        *reinterpret_cast<u32x4_t*>(tile + chunk_off<G>(n, c)) = convert(raw[i]);
       }
     }
   }
 };
 
+// Direct global->LDS staging (global_load_lds_dwordx4) for keys already in the MFMA element
+// format: no staging registers. Each load instruction of a wave fills 1 KB of LDS, lane i
+// writing bytes [16 i, 16 i + 16); the lane therefore fetches the global chunk that the
+// swizzled layout puts at that position. Invalid keys fetch key row 0 of the sequence (finite
+// data whose scores are never stored). Completion: s_waitcnt vmcnt(0) before the barrier.
+template <int D, int NTHR, int KT>
+struct DirectLoader {
+  typedef Geo<MmaBf16, D, KT> G;
+  static constexpr int NCH = KT * G::CPR;
+  static constexpr int NWAVE = NTHR / 64;
+  static constexpr int ITERS = NCH / NTHR > 0 ? NCH / NTHR : 1;
+
+  // key row and logical chunk that this lane's i-th load fills
+  __device__ __forceinline__ static int phys(int i, int wave, int lane) {
+    return (i * NWAVE + wave) * 64 + lane;
+  }
+  __device__ __forceinline__ static int row_of(int i, int wave, int lane) {
+    return phys(i, wave, lane) / G::CPR;
+  }
+  __device__ __forceinline__ static bool first_chunk(int i, int wave, int lane) {
+    return phys(i, wave, lane) % G::CPR == 0;
+  }
+
+  // kidx[i]: key index (row of the sequence's key array) of row_of(i), or -1 for an unused row
+  template <int N>
+  __device__ __forceinline__ static void load_idx(const uint8_t* kseq, uint8_t* tile, int wave,
+                                                  int lane, const int (&kidx)[N]) {
+    static_assert(NCH % NTHR == 0 && N == ITERS, "tile chunks must divide over the work-group");
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const int blk = i * NWAVE + wave;              // 1 KB LDS block written by this instr
+      const int p = blk * 64 + lane;
+      const int n = p / G::CPR, cp = p % G::CPR;
+      const int c = cp ^ (n & G::SWZ);               // logical chunk stored at p
+      const int ki = kidx[i];
+      const uint8_t* src = kseq + (int64_t)(ki >= 0 ? ki : 0) * G::ROW_BYTES + c * 16;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                                reinterpret_cast<uintptr_t>(tile + blk * 1024)),
+                                       16, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ReLU through an integer max: an IEEE float is negative iff its bit pattern is negative as an
+// int32, so max(bits, 0) is bits(x) for x >= +0 and +0 otherwise (one VALU op, no NaN quieting).
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // One wave: x = q(32*HB heads) . k(32 keys of the tile starting at row n0) accumulated in acc.
-template <class Mma, int D, int HB>
-__device__ __forceinline__ void tile_mma(const typename Mma::frag_t (&qf)[HB][Geo<Mma, D>::NKK],
+template <class Mma, int D, int HB, int KT>
+__device__ __forceinline__ void tile_mma(const typename Mma::frag_t (&qf)[HB][Geo<Mma, D, KT>::NKK],
                                          const uint8_t* tile, int n0, int lane,
                                          f32x16_t (&acc)[HB]) {
-  typedef Geo<Mma, D> G;
+  typedef Geo<Mma, D, KT> G;
   const int hh = lane >> 5;
   const int n = n0 + (lane & 31);
-  const uint8_t* krow = tile + n * G::ROW_BYTES;
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16_t{};
   if constexpr (Mma::E == 8) {
     bf16x8_t bf[G::NKK];
 #pragma unroll
     for (int kk = 0; kk < G::NKK; ++kk)
-      bf[kk] = *reinterpret_cast<const bf16x8_t*>(
-          krow + (((hh * (G::CPR / 2) + kk) ^ (n & G::SWZ)) << 4));
+      bf[kk] = *reinterpret_cast<const bf16x8_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + kk));
 #pragma unroll
-    for (int kk = 0; kk < G::NKK; ++kk)
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = Mma::mma(qf[hb][0], bf[0], f32x16_t{});
+#pragma unroll
+    for (int kk = 1; kk < G::NKK; ++kk)
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) acc[hb] = Mma::mma(qf[hb][kk], bf[kk], acc[hb]);
   } else {
 #pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16_t{};
+#pragma unroll
     for (int c4 = 0; c4 < G::NKK / 4; ++c4) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(
-          krow + (((hh * (G::CPR / 2) + c4) ^ (n & G::SWZ)) << 4));
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + c4));
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -132,16 +188,53 @@ __device__ __forceinline__ void tile_mma(const typename Mma::frag_t (&qf)[HB][Ge
   }
 }
 
+// B fragments (the 32 keys' halves of the head dimension) of one 32-key step, bf16 path.
+template <int D, int KT>
+__device__ __forceinline__ void load_bfrag(const uint8_t* tile, int n0, int lane,
+                                           bf16x8_t (&bf)[Geo<MmaBf16, D, KT>::NKK]) {
+  typedef Geo<MmaBf16, D, KT> G;
+  const int hh = lane >> 5;
+  const int n = n0 + (lane & 31);
+#pragma unroll
+  for (int kk = 0; kk < G::NKK; ++kk)
+    bf[kk] = *reinterpret_cast<const bf16x8_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + kk));
+}
+
+// bf16 path: MFMAs of one 32-key step from fragments already in registers; when `next` is
+// set, each fragment register is refilled with the next step's fragment right after its last
+// use, so that the LDS latency of the next step hides behind this step's MFMAs.
+template <int D, int HB, int KT>
+__device__ __forceinline__ void tile_mma_rot(const bf16x8_t (&qf)[HB][Geo<MmaBf16, D, KT>::NKK],
+                                             bf16x8_t (&bf)[Geo<MmaBf16, D, KT>::NKK],
+                                             const uint8_t* tile, int next_n0, bool next, int lane,
+                                             f32x16_t (&acc)[HB]) {
+  typedef Geo<MmaBf16, D, KT> G;
+  const int hh = lane >> 5;
+  const int n = next_n0 + (lane & 31);
+#pragma unroll
+  for (int kk = 0; kk < G::NKK; ++kk) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+      acc[hb] = MmaBf16::mma(qf[hb][kk], bf[kk], kk == 0 ? f32x16_t{} : acc[hb]);
+    if (next)
+      bf[kk] = *reinterpret_cast<const bf16x8_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + kk));
+  }
+}
+
 // ReLU + head-weighted sum of one 32x32 tile per head block; returns the full score of key
-// (lane % 32) in every lane.
+// (lane % 32) in every lane (lanes l and l+32 hold complementary heads; the permlane32 swap
+// exchanges the halves so that both lanes end with the same total).
 template <int HB>
 __device__ __forceinline__ float tile_epilogue(const f32x16_t (&acc)[HB], const float (&wv)[HB][16]) {
-  float part = 0.f;
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part = fmaf(wv[hb][r], fmaxf(acc[hb][r], 0.f), part);
-  return part + __shfl_xor(part, 32, 64);
+    for (int r = 0; r < 16; ++r) p[r & 3] = fmaf(wv[hb][r], relu(acc[hb][r]), p[r & 3]);
+  const float part = (p[0] + p[1]) + (p[2] + p[3]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                   false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 }  // namespace idx
