@@ -18,9 +18,10 @@
  *   - The caller owns all buffers. Scratch memory is the caller's `ws` buffer of `ws_bytes`
  *     bytes, at least idx_workspace_bytes(...) for the same arguments.
  *   - Output rows hold a SET of token indices: the first n = min(k, visible candidates) entries
- *     are distinct token indices (within the sequence, 0..N-1) in ascending order, the rest are
- *     -1; out_score (optional, may be NULL) holds the fp32 score of each index and -inf for the
- *     padding. When several tokens tie with the k-th best score, the lowest indices are kept.
+ *     are distinct token indices (within the sequence, 0..N-1) in unspecified order, the rest
+ *     are -1; out_score (optional, may be NULL) holds the fp32 score of each index and -inf for
+ *     the padding. When several tokens tie with the k-th best score, the lowest indices are kept,
+ *     so the set is deterministic.
  *   - Return value: IDX_OK or a negative IDX_ERR_* code. Argument errors are detected before
  *     anything is enqueued. Device-array contents are preconditions and are not checked:
  *     0 <= k_len[b] <= N, keys and queries finite, fp8 scales >= 0 and finite.
@@ -96,8 +97,8 @@ int idx_score_topk(const idx_problem* p, int32_t k, int32_t* out_idx, float* out
  * Every member then scores the candidates inside its own prefix with its own query and weights
  * and keeps its top k.
  *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
- *   out_cand [B, ceil(T/group_size), n_cand] int32 (optional): each group's candidates,
- *            ascending, -1 padded.
+ *   out_cand [B, ceil(T/group_size), n_cand] int32 (optional): each group's candidates in
+ *            ascending token order, -1 padded.
  * With n_cand >= the prefix length the result equals idx_score_topk's. Requires n_cand <= N. */
 int idx_group_proxy_refine(const idx_problem* p, int32_t k, int32_t group_size, int32_t n_cand,
                            int32_t* out_idx, float* out_score, int32_t* out_cand,
@@ -110,7 +111,8 @@ int idx_group_proxy_refine(const idx_problem* p, int32_t k, int32_t group_size, 
  * first token is in its prefix (same score formula), keeps its n_blocks_keep best blocks, then
  * scores the tokens of the kept blocks inside its prefix and keeps its top k.
  *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
- *   out_blocks [B, T, n_blocks_keep] int32 (optional): kept block ids, ascending, -1 padded.
+ *   out_blocks [B, T, n_blocks_keep] int32 (optional): kept block ids in ascending order, -1
+ *              padded.
  * Keys must be IDX_BF16 or IDX_F32 (IDX_ERR_UNSUPPORTED for fp8). Requires
  * ceil(N / block_size) <= 65536 and n_blocks_keep <= 32767. With n_blocks_keep >= the number of
  * eligible blocks the result equals idx_score_topk's. */

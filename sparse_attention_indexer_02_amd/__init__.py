@@ -11,7 +11,8 @@ error (there is no other implementation to fall back to).
 
 Shapes: q [B,T,H,D] (bf16 or fp32), k [B,N,D] (bf16, fp32, or float8_e4m3fn / uint8 E4M3FN
 bytes with k_scale [B,N] fp32), w [B,T,H] fp32, q_pos [B,T] int32, k_len [B] int32 or None.
-Outputs: int32 [B,T,topk] token indices (ascending, -1 padded) and fp32 scores (-inf padded).
+Outputs: int32 [B,T,topk] token-index sets (order within a row unspecified, -1 padded) and the
+matching fp32 scores (-inf padded).
 """
 from __future__ import annotations
 

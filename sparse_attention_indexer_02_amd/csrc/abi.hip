@@ -20,6 +20,8 @@ constexpr size_t kScoreBudget = size_t(1) << 30;     // score rows held per chun
 constexpr int kTargetGroups = 1024;                  // work-groups wanted per score launch
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+// score-row stride (floats): rows start 256-byte aligned so that the selector can use 16-byte loads
+int64_t rstride(int64_t n) { return (n + 63) / 64 * 64; }
 
 // ---------------------------------------------------------------------------------------------
 // kernel timing (idx_timer_enable / idx_timer_read)
@@ -115,15 +117,17 @@ struct DensePlan {
   int chunkT;
   float* scores;
   int32_t* row_len;
+  int32_t* meta;
   size_t bytes;
 };
 
 DensePlan plan_dense(const idx_problem* p, void* ws) {
   DensePlan d;
   Carver c(ws);
-  d.chunkT = chunk_rows(p->B, (int64_t)p->N * 4, p->T);
-  d.scores = c.take<float>((size_t)p->B * d.chunkT * p->N);
+  d.chunkT = chunk_rows(p->B, rstride(p->N) * 4, p->T);
+  d.scores = c.take<float>((size_t)p->B * d.chunkT * rstride(p->N));
   d.row_len = c.take<int32_t>((size_t)p->B * d.chunkT);
+  d.meta = c.take<int32_t>((size_t)p->B * d.chunkT * 4);
   d.bytes = c.off + kAlign;
   return d;
 }
@@ -138,6 +142,7 @@ struct GroupPlan {
   int32_t* cand_cnt;
   float* mscores;
   int32_t* row_len;
+  int32_t* meta;
   size_t bytes;
 };
 
@@ -149,13 +154,14 @@ GroupPlan plan_group(const idx_problem* p, int G, int C, void* ws, int32_t* out_
   g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
   g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
   g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
-  g.chunkP = chunk_rows(p->B, (int64_t)p->N * 4, g.NG);
-  g.pscores = c.take<float>((size_t)p->B * g.chunkP * p->N);
+  g.chunkP = chunk_rows(p->B, rstride(p->N) * 4, g.NG);
+  g.pscores = c.take<float>((size_t)p->B * g.chunkP * rstride(p->N));
   g.cand = out_cand ? out_cand : c.take<int32_t>((size_t)p->B * g.NG * C);
   g.cand_cnt = c.take<int32_t>((size_t)p->B * g.NG);
-  g.chunkG = chunk_rows(p->B, (int64_t)G * C * 4, g.NG);
-  g.mscores = c.take<float>((size_t)p->B * std::min(p->T, g.chunkG * G) * C);
+  g.chunkG = chunk_rows(p->B, (int64_t)G * rstride(C) * 4, g.NG);
+  g.mscores = c.take<float>((size_t)p->B * std::min(p->T, g.chunkG * G) * rstride(C));
   g.row_len = c.take<int32_t>((size_t)p->B * std::max(std::min(p->T, g.chunkG * G), g.chunkP));
+  g.meta = c.take<int32_t>((size_t)p->B * std::max(std::min(p->T, g.chunkG * G), g.chunkP) * 4);
   g.bytes = c.off + kAlign;
   return g;
 }
@@ -168,6 +174,7 @@ struct BlockPlan {
   int32_t* n_kept;
   float* rscores;
   int32_t* row_len;
+  int32_t* meta;
   size_t bytes;
 };
 
@@ -177,13 +184,14 @@ BlockPlan plan_block(const idx_problem* p, int Bs, int keep, void* ws, int32_t* 
   b.NB = (p->N + Bs - 1) / Bs;
   const size_t keb = p->k_dtype == IDX_BF16 ? 2 : 4;
   b.pooled = c.take<uint8_t>((size_t)p->B * b.NB * p->D * keb);
-  b.chunkT1 = chunk_rows(p->B, (int64_t)b.NB * 4, p->T);
-  b.cscores = c.take<float>((size_t)p->B * b.chunkT1 * b.NB);
+  b.chunkT1 = chunk_rows(p->B, rstride(b.NB) * 4, p->T);
+  b.cscores = c.take<float>((size_t)p->B * b.chunkT1 * rstride(b.NB));
   b.blocks = out_blocks ? out_blocks : c.take<int32_t>((size_t)p->B * p->T * keep);
   b.n_kept = c.take<int32_t>((size_t)p->B * p->T);
-  b.chunkT2 = chunk_rows(p->B, (int64_t)keep * Bs * 4, p->T);
-  b.rscores = c.take<float>((size_t)p->B * b.chunkT2 * keep * Bs);
+  b.chunkT2 = chunk_rows(p->B, rstride((int64_t)keep * Bs) * 4, p->T);
+  b.rscores = c.take<float>((size_t)p->B * b.chunkT2 * rstride((int64_t)keep * Bs));
   b.row_len = c.take<int32_t>((size_t)p->B * std::max(b.chunkT1, b.chunkT2));
+  b.meta = c.take<int32_t>((size_t)p->B * std::max(b.chunkT1, b.chunkT2) * 4);
   b.bytes = c.off + kAlign;
   return b;
 }
@@ -207,7 +215,10 @@ ScoreArgs base_score_args(const idx_problem* p) {
   return a;
 }
 
-hipError_t run_score(ScoreArgs& a, int n_keys_max, hipStream_t s) {
+// Launches the score kernel; when the key range is not split, the kernel also writes each row's
+// selection summary into `meta` for the selector, and *fused is set.
+hipError_t run_score(ScoreArgs& a, int n_keys_max, int topk_k, int32_t* meta, bool* fused,
+                     hipStream_t s) {
   const int qt = score_queries_per_tile(a.H);
   if (a.mode == MODE_RANGE) {
     a.tiles_per_seq = (a.c1 - a.c0 + qt - 1) / qt;
@@ -215,6 +226,10 @@ hipError_t run_score(ScoreArgs& a, int n_keys_max, hipStream_t s) {
     a.tiles_per_seq = (a.c1 - a.c0) * ((a.group_size + qt - 1) / qt);
   }
   const int nsplit = key_split(a.B * a.tiles_per_seq, n_keys_max, &a.split_keys);
+  *fused = nsplit == 1 && meta != nullptr;
+  a.row_meta = *fused ? meta : nullptr;
+  a.topk_k = topk_k;
+  a.digit_bits = n_keys_max < 65536 ? 12 : 11;
   return timed("score", s, [&] { return launch_score(a, nsplit, s); });
 }
 
@@ -248,11 +263,14 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
     const int c1 = std::min(p->T, c0 + pl.chunkT);
     ScoreArgs a = base_score_args(p);
     a.c0 = c0; a.c1 = c1;
-    a.scores = pl.scores; a.score_stride = p->N; a.row_len = pl.row_len;
+    a.scores = pl.scores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
-    if ((st = from_hip(run_score(a, p->N, s)))) return st;
-    TopkArgs t = topk_args(pl.scores, p->N, pl.row_len, p->B * (c1 - c0), k, c1 - c0, p->T, c0,
+    bool fused;
+    if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s)))) return st;
+    TopkArgs t = topk_args(pl.scores, rstride(p->N), pl.row_len, p->B * (c1 - c0), k, c1 - c0, p->T, c0,
                            out_idx, out_score, k);
+    t.row_meta = fused ? pl.meta : nullptr;
+    t.digit_bits = a.digit_bits;
     if ((st = from_hip(run_topk(t, p->N, s)))) return st;
   }
   return IDX_OK;
@@ -280,14 +298,22 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
     ScoreArgs a = base_score_args(p);
     a.q = pl.pq; a.w = pl.pw; a.q_pos = pl.ppos; a.T = pl.NG;
     a.c0 = c0; a.c1 = c1;
-    a.scores = pl.pscores; a.score_stride = p->N; a.row_len = pl.row_len;
+    a.scores = pl.pscores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
-    if ((st = from_hip(run_score(a, p->N, s)))) return st;
-    TopkArgs t = topk_args(pl.pscores, p->N, pl.row_len, p->B * (c1 - c0), C, c1 - c0, pl.NG, c0,
+    bool fused;
+    if ((st = from_hip(run_score(a, p->N, C, pl.meta, &fused, s)))) return st;
+    TopkArgs t = topk_args(pl.pscores, rstride(p->N), pl.row_len, p->B * (c1 - c0), C, c1 - c0, pl.NG, c0,
                            pl.cand, nullptr, C);
     t.out_count = pl.cand_cnt;
+    t.row_meta = fused ? pl.meta : nullptr;
+    t.digit_bits = a.digit_bits;
     if ((st = from_hip(run_topk(t, p->N, s)))) return st;
   }
+  // candidate lists in ascending token order (the refine indexes them by slot)
+  if ((st = from_hip(timed("sort", s, [&] {
+         return launch_sort_rows(pl.cand, C, pl.cand_cnt, p->B * pl.NG, C, s);
+       }))))
+    return st;
   // per-member refine over the group's candidates
   for (int g0 = 0; g0 < pl.NG; g0 += pl.chunkG) {
     const int g1 = std::min(pl.NG, g0 + pl.chunkG);
@@ -297,11 +323,14 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
     a.list = pl.cand; a.list_len = pl.cand_cnt; a.list_stride = C; a.group_size = G;
     a.n_groups = pl.NG;
     a.c0 = g0; a.c1 = g1;
-    a.scores = pl.mscores; a.score_stride = C; a.row_len = pl.row_len;
+    a.scores = pl.mscores; a.score_stride = rstride(C); a.row_len = pl.row_len;
     a.rows_per_seq = rows;
-    if ((st = from_hip(run_score(a, C, s)))) return st;
-    TopkArgs t = topk_args(pl.mscores, C, pl.row_len, p->B * rows, k, rows, p->T, g0 * G, out_idx,
+    bool fused;
+    if ((st = from_hip(run_score(a, C, k, pl.meta, &fused, s)))) return st;
+    TopkArgs t = topk_args(pl.mscores, rstride(C), pl.row_len, p->B * rows, k, rows, p->T, g0 * G, out_idx,
                            out_score, k);
+    t.row_meta = fused ? pl.meta : nullptr;
+    t.digit_bits = a.digit_bits;
     t.map_mode = MAP_LIST;
     t.list = pl.cand; t.list_stride = C; t.group_size = G; t.n_groups = pl.NG;
     if ((st = from_hip(run_topk(t, C, s)))) return st;
@@ -335,14 +364,21 @@ int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_
     a.keys = pl.pooled; a.k_scale = nullptr; a.key_cap = pl.NB;
     a.pos_stride = Bs; a.count_div = Bs;
     a.c0 = c0; a.c1 = c1;
-    a.scores = pl.cscores; a.score_stride = pl.NB; a.row_len = pl.row_len;
+    a.scores = pl.cscores; a.score_stride = rstride(pl.NB); a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
-    if ((st = from_hip(run_score(a, pl.NB, s)))) return st;
-    TopkArgs t = topk_args(pl.cscores, pl.NB, pl.row_len, p->B * (c1 - c0), keep, c1 - c0, p->T,
+    bool fused;
+    if ((st = from_hip(run_score(a, pl.NB, keep, pl.meta, &fused, s)))) return st;
+    TopkArgs t = topk_args(pl.cscores, rstride(pl.NB), pl.row_len, p->B * (c1 - c0), keep, c1 - c0, p->T,
                            c0, pl.blocks, nullptr, keep);
     t.out_count = pl.n_kept;
+    t.row_meta = fused ? pl.meta : nullptr;
+    t.digit_bits = a.digit_bits;
     if ((st = from_hip(run_topk(t, pl.NB, s)))) return st;
   }
+  if ((st = from_hip(timed("sort", s, [&] {
+         return launch_sort_rows(pl.blocks, keep, pl.n_kept, p->B * p->T, keep, s);
+       }))))
+    return st;
   // token refine inside the kept blocks
   const int qt = score_queries_per_tile(p->H);
   for (int c0 = 0; c0 < p->T; c0 += pl.chunkT2) {
@@ -353,12 +389,13 @@ int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_
     r.B = p->B; r.T = p->T; r.H = p->H; r.D = p->D; r.N = p->N;
     r.blocks = pl.blocks; r.n_kept = pl.n_kept; r.keep_stride = keep; r.block_size = Bs;
     r.t0 = c0; r.t1 = c1;
-    r.scores = pl.rscores; r.score_stride = (int64_t)keep * Bs;
+    r.scores = pl.rscores; r.score_stride = rstride((int64_t)keep * Bs);
     r.row_len = pl.row_len; r.rows_per_seq = c1 - c0;
+    r.row_meta = nullptr; r.topk_k = k;
     r.tiles_per_seq = (c1 - c0 + qt - 1) / qt;
     if ((st = from_hip(timed("block_refine", s, [&] { return launch_block_refine(r, s); }))))
       return st;
-    TopkArgs t = topk_args(pl.rscores, (int64_t)keep * Bs, pl.row_len, p->B * (c1 - c0), k,
+    TopkArgs t = topk_args(pl.rscores, rstride((int64_t)keep * Bs), pl.row_len, p->B * (c1 - c0), k,
                            c1 - c0, p->T, c0, out_idx, out_score, k);
     t.map_mode = MAP_BLOCKS;
     t.blocks = pl.blocks; t.blocks_stride = keep; t.block_size = Bs;

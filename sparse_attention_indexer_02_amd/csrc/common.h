@@ -76,6 +76,7 @@ __device__ __forceinline__ float key2f(uint32_t k) {
   return __uint_as_float(u);
 }
 constexpr uint32_t KEY_NONE = 0u;
+constexpr uint32_t KEY_NEG_INF = 0x007FFFFFu;    // f2key(-inf): slots without a candidate
 
 // ---------------------------------------------------------------------------------------------
 // MFMA flavours. Elements live in LDS in the flavour's element type.
@@ -142,6 +143,79 @@ __device__ __forceinline__ T wave_incl_scan(T v) {
     if (l >= o) v += u;
   }
   return v;
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP (row shifts, then row broadcasts): no LDS
+// round trips.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_bcast(uint32_t x, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
+// Wave-level search over a histogram of nbins (multiple of 64) bins, highest bin first: the bin
+// holding the need-th largest element (need >= 1) and the count in higher bins. count(b) reads
+// bin b. Returns the total count; *bin_out = -1 when need exceeds it.
+template <class CountFn>
+__device__ __forceinline__ uint32_t wave_hist_find(int nbins, uint32_t need, CountFn count,
+                                                   int* bin_out, uint32_t* above_out) {
+  const int lane = lane_id();
+  const int per = nbins / 64;
+  const int hi = nbins - 1 - lane * per;
+  uint32_t sum = 0;
+  for (int i = 0; i < per; ++i) sum += count(hi - i);
+  const uint32_t inc = wave_scan_dpp(sum);
+  const uint32_t tot = wave_bcast(inc, 63);
+  int bin = -1;
+  uint32_t run = inc - sum;
+  if (need > 0 && run < need && need <= inc) {
+    for (int i = 0; i < per; ++i) {
+      const uint32_t h = count(hi - i);
+      if (run + h >= need) {
+        bin = hi - i;
+        break;
+      }
+      run += h;
+    }
+  }
+  const uint64_t m = __ballot(bin >= 0);
+  if (m) {
+    const int src = __builtin_ctzll(m);
+    *bin_out = (int)wave_bcast((uint32_t)bin, src);
+    *above_out = wave_bcast(run, src);
+  } else {
+    *bin_out = -1;
+    *above_out = 0;
+  }
+  return tot;
+}
+
+__device__ __forceinline__ uint32_t wave_hist_find(const uint32_t* hist, int nbins, uint32_t need,
+                                                   int* bin_out, uint32_t* above_out) {
+  return wave_hist_find(nbins, need, [&](int b) { return hist[b]; }, bin_out, above_out);
+}
+
+// First radix digit of a selection: the top `bits` (11 or 12) bits of the order-preserving key.
+// With 12 bits the 4096 counters are 16-bit halves of 2048 words (valid for rows of fewer than
+// 65536 slots, so that no half can carry into its neighbour).
+__device__ __forceinline__ uint32_t digit1(uint32_t key, int bits) { return key >> (32 - bits); }
+
+__device__ __forceinline__ void hist1_add(uint32_t* words, uint32_t key, int bits) {
+  if (bits == 12) atomicAdd(&words[key >> 21], 1u << (((key >> 20) & 1u) * 16));
+  else atomicAdd(&words[key >> 21], 1u);
+}
+
+__device__ __forceinline__ uint32_t hist1_count(const uint32_t* words, int bin, int bits) {
+  if (bits == 12) return (words[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu;
+  return words[bin];
 }
 
 }  // namespace idx

@@ -30,18 +30,28 @@ struct ScoreArgs {
   int c0, c1;                      // RANGE: query range [c0,c1); LIST: group range [c0,c1)
   float* scores; int64_t score_stride;
   int32_t* row_len;                // slots per row, written by split 0
+  int32_t* row_meta;               // optional [rows][4] selection summary (needs one key split)
+  int topk_k;                      // selection size the summary is computed for
+  int digit_bits;                  // width of the summary's radix digit (11, or 12 for rows < 65536)
   int rows_per_seq;                // score rows per sequence in this chunk
   int tiles_per_seq;
   int split_keys;                  // keys per grid.y split (multiple of the key tile)
 };
 
-// Pick rows from per-row score arrays: the top-k slots of each row, written in ascending slot
-// order (= ascending token order for every slot map used here).
+// Pick rows from per-row score arrays: the top-k slots of each row (a set; with a row summary
+// from the score kernel the order within the row is unspecified, otherwise ascending).
 enum { MAP_IDENT = 0, MAP_LIST = 1, MAP_BLOCKS = 2 };
+
+// Row selection summary written by a score kernel next to each score row (first radix digit, 11
+// or 12 bits, of the order-preserving key image): {finite slots, bin of the k-th largest key or -1 when every
+// finite slot is selected, slots in higher bins, slots in that bin}.
+enum { META_NVALID = 0, META_BIN = 1, META_ABOVE = 2, META_INBIN = 3 };
 
 struct TopkArgs {
   const float* scores; int64_t score_stride;
   const int32_t* row_len;
+  const int32_t* row_meta;         // optional: summaries from the score kernel
+  int digit_bits;                  // their radix digit width
   int n_rows, k;
   int rows_per_seq, T_out, t_off;  // output row = (r / rows_per_seq) * T_out + t_off + r % rows_per_seq
   int32_t* out_idx; float* out_score; int out_stride;
@@ -71,6 +81,7 @@ struct BlockRefineArgs {
   int t0, t1;                            // query range of this chunk
   float* scores; int64_t score_stride;   // slot = kept position * block_size + offset
   int32_t* row_len; int rows_per_seq; int tiles_per_seq;
+  int32_t* row_meta; int topk_k;
 };
 
 hipError_t launch_score(const ScoreArgs& a, int n_splits, hipStream_t s);
@@ -78,6 +89,8 @@ hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_block_refine(const BlockRefineArgs& a, hipStream_t s);
+hipError_t launch_sort_rows(int32_t* rows, int stride, const int32_t* count, int n_rows, int max_count,
+                            hipStream_t s);
 bool score_supported(int q_dtype, int k_dtype, int H, int D);
 
 constexpr int KEY_TILE = 64;       // keys per LDS tile of the score kernels

@@ -41,6 +41,10 @@ score_kernel(ScoreArgs a) {
   float* sscale = reinterpret_cast<float*>(skey + 2 * KT);                 // [2][KT]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // per-wave histogram of the first radix digit of the row's order-preserving score keys, from
+  // which the wave writes its row's selection summary (the selector's first radix pass)
+  uint32_t* whist = reinterpret_cast<uint32_t*>(sscale + 2 * KT) + wave * 2048;
+  const bool fuse = a.row_meta != nullptr;
   const int lin = gridDim.x - 1 - blockIdx.x;       // heaviest tiles first
   const int b = lin % a.B;
   const int ti = lin / a.B;
@@ -84,6 +88,8 @@ score_kernel(ScoreArgs a) {
   const int kb1 = min(key_end, kb0 + a.split_keys);
   if (kb0 >= kb1) return;                           // uniform over the work-group
   const int lim = min(my_count, kb1);               // this wave's last slot (exclusive)
+  if (fuse)
+    for (int i = lane; i < 2048; i += 64) whist[i] = 0u;
 
   // query fragments and head weights of this wave's query
   typename Mma::frag_t qf[HB][G::NKK];
@@ -247,10 +253,28 @@ score_kernel(ScoreArgs a) {
             if (skey[cur * KT + n] > my_pos) v = -INFINITY;
           }
           srow[base + n] = v;
+          if (fuse) {
+            const uint32_t key = f2key(v);
+            if (key > KEY_NEG_INF) hist1_add(whist, key, a.digit_bits);
+          }
         }
       }
     }
     __syncthreads();
+  }
+  if (fuse && active) {
+    int bin;
+    uint32_t above;
+    const int bits = a.digit_bits;
+    const uint32_t tot = wave_hist_find(1 << bits, (uint32_t)a.topk_k,
+                                        [&](int q) { return hist1_count(whist, q, bits); }, &bin, &above);
+    if (lane == 0) {
+      int32_t* m = a.row_meta + ((int64_t)b * a.rows_per_seq + (t - row0)) * 4;
+      m[META_NVALID] = (int32_t)tot;
+      m[META_BIN] = bin;
+      m[META_ABOVE] = (int32_t)above;
+      m[META_INBIN] = bin >= 0 ? (int32_t)hist1_count(whist, bin, bits) : 0;
+    }
   }
 }
 
@@ -270,7 +294,8 @@ static hipError_t launch_one(const ScoreArgs& a, int n_splits, hipStream_t s) {
   constexpr int NW = WavesFor<HB>::value;
   constexpr int KT = TileKeys<Mma, KST>::value;
   typedef Geo<Mma, D, KT> G;
-  const size_t lds = 2 * G::TILE_BYTES + 4 * KT * sizeof(int32_t);
+  const size_t lds = 2 * G::TILE_BYTES + 4 * KT * sizeof(int32_t) +
+                     (a.row_meta ? (size_t)NW * 2048 * sizeof(uint32_t) : 0);
   auto kfn = a.mode == MODE_LIST ? score_kernel<Mma, D, HB, KST, true>
                                  : score_kernel<Mma, D, HB, KST, false>;
   if (lds > 65536) {

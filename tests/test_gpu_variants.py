@@ -37,6 +37,7 @@ def check_group(prob, k, G, C, gi, gs, gc, groups, name):
                         ps["proxy_magnitude"], C, prob.D, ctx=f"{name} cand b{b} g{g}",
                         oracle_sel=ps["cand"])
         cand = gc[b, g, :ps["n_cand"]].astype(np.int64)
+        assert (np.diff(cand) > 0).all() and (gc[b, g, ps["n_cand"]:] == -1).all()
         for t in oracle.group_members(prob.T, G, g):
             d = oracle.dense_row(inp, b, t, k)
             uni = cand[cand < inp.P(b, t)]
@@ -123,6 +124,7 @@ def check_block(prob, k, Bs, keep, gi, gs, gb, rows, name):
                         r["block_magnitude"], keep, prob.D, ctx=f"{name} blocks b{b} t{t}",
                         oracle_sel=r["blocks"])
         kept = gb[b, t, :min(keep, n_elig)].astype(np.int64)
+        assert (np.diff(kept) > 0).all() and (gb[b, t, min(keep, n_elig):] == -1).all()
         d = oracle.dense_row(inp, b, t, k)
         toks = np.sort((kept[:, None] * Bs + np.arange(Bs)[None]).reshape(-1))
         toks = toks[toks < inp.P(b, t)]
