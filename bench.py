@@ -202,7 +202,8 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
     kernels = {name: idx.timer_read(name)
-               for name in ("score", "topk", "proxy", "pool", "block_refine")}
+               for name in ("score", "topk", "sort", "proxy", "pool", "block_refine", "decode_zero",
+                            "decode_scan", "decode_select", "decode_resolve")}
     idx.timer_enable(False)
     log("[bench] per-kernel ms/step: " + ", ".join(
         f"{n} {ms / args.steps:.3f} ({c // max(1, args.steps)} launches)" for n, (ms, c) in kernels.items() if c))
@@ -213,7 +214,7 @@ def main():
     cfg = {"workload": args.workload, "B": B, "T": T, "H": prob.H, "D": prob.D, "N": prob.N,
            "k": k, "q_dtype": W.DTYPE_NAMES[prob.q_dtype], "k_dtype": W.DTYPE_NAMES[prob.k_dtype],
            "seed": args.seed, "pairs_per_step": pairs}
-    if op == "dense" and prob.k_dtype != W.FP8_E4M3:
+    if op == "dense" and kernels["decode_scan"][1] == 0:
         dom = "score"
         ms, n = kernels["score"]
         flops = dense_flops(prob)
@@ -223,10 +224,11 @@ def main():
                 "traffic": None, "per_launch": f"{flops / (n / args.steps):.4g} flop",
                 "mean_launch_ms": ms / n}
     elif op == "dense":
-        ms, n = kernels["score"]
+        # decode shape: the streaming scan is the dominant kernel, bound by the key-cache read
+        ms, n = kernels["decode_scan"]
         byts = decode_bytes(prob)
         achieved = byts / (n / args.steps) / (ms / n * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "score_kernel", "achieved": achieved,
+        roof = {"bound": "hbm", "kernel": "decode_scan_kernel", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "traffic": None, "per_launch": f"{byts / (n / args.steps):.4g} B",
                 "mean_launch_ms": ms / n}

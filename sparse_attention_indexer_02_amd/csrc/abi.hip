@@ -196,6 +196,59 @@ BlockPlan plan_block(const idx_problem* p, int Bs, int keep, void* ws, int32_t* 
   return b;
 }
 
+// Decode-shaped problems (few queries per sequence over a long cache) take the streaming path.
+bool use_decode(const idx_problem* p) {
+  return decode_supported(p->q_dtype, p->k_dtype, p->H, p->D, p->T, p->N);
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+struct DecodePlan {
+  int nchunk, chunk, sub, nsegs, cand_cap;
+  uint32_t* ccount;
+  uint32_t* cand_key;
+  uint32_t* cand_idx;
+  uint32_t* cand2_key;
+  uint32_t* cand2_idx;
+  size_t bytes;
+};
+
+DecodePlan plan_decode(const idx_problem* p, void* ws) {
+  DecodePlan d;
+  Carver c(ws);
+  const int64_t rows = (int64_t)p->B * p->T;
+  const int pairs = (p->T + 1) / 2;
+  // about one scan work-group per compute unit (each holds a whole unit's LDS), chunks of at
+  // least 1024 keys
+  int nchunk = std::max(1, (cu_count() + p->B * pairs - 1) / (p->B * pairs));
+  int chunk = (int)std::max<int64_t>(1024, ((int64_t)p->N + nchunk - 1) / nchunk);
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk > DECODE_SUB) chunk = (chunk + DECODE_SUB - 1) / DECODE_SUB * DECODE_SUB;
+  d.chunk = chunk;
+  d.nchunk = (p->N + chunk - 1) / chunk;
+  d.sub = std::min(chunk, DECODE_SUB);
+  d.nsegs = (p->N + d.sub - 1) / d.sub;
+  d.cand_cap = (int)rstride(p->N);
+  d.ccount = c.take<uint32_t>((size_t)rows * d.nsegs);
+  d.cand_key = c.take<uint32_t>((size_t)rows * d.cand_cap);
+  d.cand_idx = c.take<uint32_t>((size_t)rows * d.cand_cap);
+  d.cand2_key = c.take<uint32_t>((size_t)rows * d.cand_cap);
+  d.cand2_idx = c.take<uint32_t>((size_t)rows * d.cand_cap);
+  d.bytes = c.off + kAlign;
+  return d;
+}
+
 void* align_ws(void* ws) {
   uintptr_t u = reinterpret_cast<uintptr_t>(ws);
   return reinterpret_cast<void*>((u + kAlign - 1) / kAlign * kAlign);
@@ -252,10 +305,32 @@ TopkArgs topk_args(const float* scores, int64_t stride, const int32_t* row_len, 
 // ---------------------------------------------------------------------------------------------
 // entry points
 
+int decode_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score, void* ws,
+                size_t ws_bytes, hipStream_t s) {
+  DecodePlan pl = plan_decode(p, nullptr);
+  if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
+  pl = plan_decode(p, align_ws(ws));
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = p->q; a.w = p->w; a.q_pos = p->q_pos;
+  a.keys = p->k; a.k_dtype = p->k_dtype; a.k_scale = p->k_scale; a.k_len = p->k_len;
+  a.B = p->B; a.T = p->T; a.H = p->H; a.D = p->D; a.N = p->N;
+  a.nchunk = pl.nchunk; a.chunk = pl.chunk; a.sub = pl.sub;
+  a.ccount = pl.ccount; a.nsegs = pl.nsegs;
+  a.cand_key = pl.cand_key; a.cand_idx = pl.cand_idx;
+  a.cand2_key = pl.cand2_key; a.cand2_idx = pl.cand2_idx; a.cand_cap = pl.cand_cap;
+  a.k = k;
+  a.out_idx = out_idx; a.out_score = out_score;
+  int st;
+  if ((st = from_hip(timed("decode_scan", s, [&] { return launch_decode_scan(a, s); })))) return st;
+  return from_hip(timed("decode_select", s, [&] { return launch_decode_select(a, s); }));
+}
+
 int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
                     void* ws, size_t ws_bytes, hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
+  if (use_decode(p)) return decode_impl(p, k, out_idx, out_score, ws, ws_bytes, s);
   DensePlan pl = plan_dense(p, nullptr);
   if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
   pl = plan_dense(p, align_ws(ws));
@@ -446,7 +521,8 @@ int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
 size_t idx_workspace_bytes(int op, const idx_problem* p, int32_t k, int32_t p1, int32_t p2) {
   try {
     if (!p || p->B <= 0 || p->T <= 0 || p->H <= 0 || p->D <= 0 || p->N <= 0 || k <= 0) return 0;
-    if (op == IDX_OP_SCORE_TOPK) return plan_dense(p, nullptr).bytes;
+    if (op == IDX_OP_SCORE_TOPK)
+      return use_decode(p) ? plan_decode(p, nullptr).bytes : plan_dense(p, nullptr).bytes;
     if (op == IDX_OP_GROUP) {
       if (p1 < 1 || p2 < 1) return 0;
       return plan_group(p, p1, p2, nullptr, nullptr).bytes;

@@ -1,0 +1,700 @@
+// Decode-shaped indexer: a few multi-token-prediction queries per sequence (T <= 4) against a
+// long key cache, usually FP8 E4M3 with one fp32 scale per token. At long context the indexer's
+// scan of the cache, not the sparse attention it feeds, sets the decode time ("Multi-layer
+// Indexer", abstract; "PIVOT", abstract), so this path is built around streaming the cache from
+// HBM exactly once per step, with both queries of a step sharing every key read.
+//
+// decode_scan_kernel: work-group = (sequence, chunk of keys, pair of queries), 4 waves, one per
+//   SIMD. A wave keeps both queries' bf16 fragments (2 x 64 heads x 128) in the accumulation
+//   registers and the head weights in vector registers, so that both queries share every key
+//   load and conversion, and walks 16-key blocks of its chunk:
+//   - each lane issues 16-byte loads of its key's bytes so that the 4 lanes of a key cover one
+//     64-byte segment per instruction; PF blocks are in flight, a block is re-issued as soon as
+//     it is consumed (the loop issues no global stores, so each wait is for one block only);
+//   - FP8 -> bf16 in registers by the hardware converter (every E4M3 value is a bf16 value, so
+//     the MFMA operand is exact); the per-token scale is positive and factors out of ReLU and
+//     the head sum, so it multiplies the reduced score;
+//   - 16x16x32 bf16 MFMAs (heads = rows, keys = columns), the epilogue of the previous block
+//     (ReLU, head weights, cross-lane head sum) interleaved with them;
+//   - the fp32 scores of up to DC_SUB keys stay in LDS with a histogram of their first radix
+//     digit (12 bits of the order-preserving key). At the end of each sub-chunk the bin of the
+//     sub-chunk's own k-th largest score is found, and only the keys in that bin or above are
+//     written to the row's candidate list (at the sub-chunk's own slots, with their count). The
+//     row's top-k is inside the union of the sub-chunks' top-k, so every key the selection can
+//     take is a candidate.
+// decode_select_kernel: work-group = row. The top-k of the row's candidates (radix select over
+//   the order-preserving keys, ties to the lowest slots) and the padding.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace idx {
+
+constexpr int DC_WAVES = 4;                      // one per SIMD
+constexpr int DC_THREADS = DC_WAVES * 64;
+constexpr int DC_BINS = DECODE_BINS;             // 12-bit first digit
+constexpr int DC_KB = 16;                        // keys per block (MFMA columns)
+constexpr int DC_SUB = DECODE_SUB;               // keys per sub-chunk held in LDS
+// blocks in flight per wave (FP8 keys: 2 KB per block per wave; bf16 keys: 4 KB)
+template <int KST> constexpr int dc_pf() { return KST == DT_FP8 ? 8 : 4; }
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v_t;
+
+// Two E4M3 bytes (bytes 0-1 or 2-3 of a word) -> two bf16 in one word; exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Element placement (the same permutation of d is used for queries and keys, so dot products
+// are unchanged). Lane = 16 * g + n: n = key (B operand column) or head (A operand row), g = the
+// lane group holding 8 consecutive elements of each K=32 step s.
+//   FP8 keys:  d = 64 * (s / 2) + 16 * g + 8 * (s % 2) + e   (lane loads bytes 64 j + 16 g)
+//   bf16 keys: d = 32 * s + 8 * g + e                        (lane loads bytes 64 s + 16 g)
+template <int KST>
+__device__ __forceinline__ int frag_d0(int s, int g) {
+  return KST == DT_FP8 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
+}
+
+// Count of bin bb in a histogram of 4096 bins held as 16-bit halves of 2048 words.
+__device__ __forceinline__ uint32_t h16(const uint32_t* w, int bb) {
+  return (w[bb >> 1] >> ((bb & 1) * 16)) & 0xFFFFu;
+}
+
+template <int D, int HB, int KST, int PF>
+__global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a) {
+  constexpr int NS = D / 32;                      // K=32 MFMA steps
+  constexpr int KEB = KST == DT_FP8 ? 1 : 2;      // key bytes per element
+  constexpr int NLD = D * KEB / 64;               // 16-byte loads per lane per block
+  static_assert(PF % 2 == 0, "blocks alternate between two accumulator sets");
+  extern __shared__ __align__(16) uint8_t lds[];
+  float* ssc = reinterpret_cast<float*>(lds);                      // [2][sub] scores
+  uint32_t* hist = reinterpret_cast<uint32_t*>(lds + 8 * a.sub);   // [2][2048] 16-bit bins
+  uint32_t* misc = hist + 2 * 2048;                                // [32]
+  uint32_t* sink = misc + 32;                                      // [2][64] per-lane sinks
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int b = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
+  const int t0 = 2 * blockIdx.y;
+  const bool two = t0 + 1 < a.T;
+  const int nrows = two ? 2 : 1;
+  const int kl = a.k_len ? max(0, min(a.k_len[b], a.N)) : a.N;
+  const int64_t r0 = (int64_t)b * a.T + t0, r1 = two ? r0 + 1 : r0;
+  const int p0 = a.q_pos[r0], p1 = a.q_pos[r1];
+  const int P0 = p0 < 0 ? 0 : min(p0 + 1, kl), P1 = p1 < 0 ? 0 : min(p1 + 1, kl);
+  const int c0 = chunk * a.chunk;
+  const int c1 = min(c0 + a.chunk, max(P0, P1));
+  {
+    // sub-chunks of this chunk past the causal limit have no candidates
+    const int s_lo = c0 >= c1 ? c0 / a.sub : (c1 + a.sub - 1) / a.sub;
+    const int s_hi = min(c0 + a.chunk, a.N);
+    for (int sg = s_lo + tid; sg * a.sub < s_hi; sg += DC_THREADS) {
+      a.ccount[r0 * a.nsegs + sg] = 0u;
+      if (two) a.ccount[r1 * a.nsegs + sg] = 0u;
+    }
+  }
+  if (c0 >= c1) return;
+
+  // query fragments and head weights of both queries (a lone query is repeated): all loads
+  // first, then the fragments move to the accumulation registers (they are only MFMA operands
+  // there, which leaves the vector registers to the key stream and the epilogue)
+  bf16x8_t qf[2][HB][NS];
+  float wv[2][HB][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t rr = j == 0 ? r0 : r1;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int head = 16 * hb + n;
+      const bool ok = head < a.H;
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (rr * a.H + (ok ? head : 0)) * D;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + frag_d0<KST>(s, g));
+        qf[j][hb][s] = ok ? __builtin_bit_cast(bf16x8_t, v) : bf16x8_t{};
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * hb + 4 * g + r;
+        wv[j][hb][r] = a.w[rr * a.H + min(h, a.H - 1)] * (h < a.H ? 1.f : 0.f);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) asm volatile("" : "+a"(qf[j][hb][s]));
+
+  // uniform bases with 32-bit per-lane byte offsets (one sequence's keys stay below 2^31 bytes)
+  const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)b * a.N * (D * KEB);
+  const uint8_t* sseq = a.k_scale ? reinterpret_cast<const uint8_t*>(a.k_scale + (int64_t)b * a.N) : nullptr;
+  const uint32_t lane_koff = 16u * g;
+  const bool owner = g == 0 || (g == 1 && two);                    // lanes that emit a score
+  const int oq = (g == 1 && two) ? 1 : 0;                          // and the row they emit for
+  const int oP = oq ? P1 : P0;
+  float* my_ssc = ssc + oq * a.sub;
+  uint32_t* my_hist = hist + oq * 2048;
+  float* sink_f = reinterpret_cast<float*>(sink) + lane;            // writes of masked lanes
+  uint32_t* sink_h = sink + 64 + lane;
+
+  for (int sub0 = c0; sub0 < c1; sub0 += a.sub) {
+    const int sub1 = min(sub0 + a.sub, c1);
+    for (int i = tid; i < 2 * 2048; i += DC_THREADS) hist[i] = 0u;
+    __syncthreads();
+
+    // ---- scores of the sub-chunk into LDS
+    const int nblk = (sub1 - sub0 + DC_KB - 1) / DC_KB;
+    const int per_wave = (nblk + DC_WAVES - 1) / DC_WAVES;
+    const int iters = (per_wave + PF - 1) / PF * PF;               // extra blocks are masked
+    // slot u of raw holds the bytes of a block from its issue until its MFMAs; slot u of scl
+    // holds a block's scale until its epilogue, one slot later, so that no loaded register is
+    // ever copied (a copy would wait for the load)
+    u32x4_t raw[PF][NLD];
+    float scl[PF];
+    auto key_of = [&](int i) {
+      const int blk = min(i * DC_WAVES + wave, nblk - 1);           // clamped: always issued
+      return min(sub0 + blk * DC_KB + n, kl - 1);
+    };
+    auto issue_keys = [&](int i, u32x4_t (&dst)[NLD]) {
+      const uint32_t off = (uint32_t)key_of(i) * (D * KEB) + lane_koff;
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        dst[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kseq + off + 64 * j));
+    };
+    auto issue_scale = [&](int i, float& sc) {
+      if constexpr (KST == DT_FP8) sc = *reinterpret_cast<const float*>(sseq + (uint32_t)key_of(i) * 4u);
+      else sc = 1.f;
+    };
+    // the previous sub-chunk's candidate stores are complete here, so that the block loop
+    // below only ever waits for its own, in-order loads; the prologue issues in the loop's
+    // order (slot u: keys of its block, then the scale of the previous slot's block)
+    __builtin_amdgcn_s_waitcnt(0x0F70);                            // vmcnt(0)
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int up = (u + PF - 1) % PF;
+      issue_keys(u, raw[u]);
+      issue_scale(up, scl[up]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    f32x4v_t acc[2][2][HB];                                        // [set][query][head block]
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) acc[x][j][hb] = f32x4v_t{};
+
+    // Epilogue of a block in pieces that the slot loop spreads between the MFMAs of the next
+    // block (a wave issues in order, so its VALU work overlaps the matrix core only when it sits
+    // between MFMAs). Pieces 0 .. NE-1: ReLU and head weight of one accumulator element (query
+    // q, head block hb, row r), in the order the MFMAs produced them; then the head sum over the
+    // 4 lane groups, the scale, the LDS store and the histogram.
+    constexpr int NE = 2 * HB * 4;
+    constexpr int NPIECE = NE + 4;
+    struct Epi {
+      float p[2][4];
+      float x[2];
+    };
+    auto piece = [&](int k, Epi& st, int i, const f32x4v_t (&ac)[2][HB], float sc) {
+      if (k < NE) {
+        const int q = k & 1, hb = (k >> 1) % HB, r = k / (2 * HB);
+        const float t = __int_as_float(max(__float_as_int(ac[q][hb][r]), 0));
+        st.p[q][r] = hb == 0 ? wv[q][hb][r] * t : fmaf(wv[q][hb][r], t, st.p[q][r]);
+      } else if (k == NE) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) st.x[q] = (st.p[q][0] + st.p[q][1]) + (st.p[q][2] + st.p[q][3]);
+      } else if (k == NE + 1) {
+        // sum of both swap outputs: the pair's total in every lane, whichever way it swaps
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(st.x[q]), __float_as_uint(st.x[q]), false, false);
+          st.x[q] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+        }
+      } else if (k == NE + 2) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.x[q]), __float_as_uint(st.x[q]), false, false);
+          st.x[q] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+        }
+      } else {
+        // branch-free (a branch would end the interleave): masked lanes write to their own sink
+        // words; a block before the first (i = -1) has a negative offset
+        const float v = (g == 1 ? st.x[1] : st.x[0]) * sc;
+        const int jl = (i * DC_WAVES + wave) * DC_KB + n;             // offset in the sub-chunk
+        const bool valid = owner & ((unsigned)jl < (unsigned)(sub1 - sub0));
+        *(valid ? my_ssc + jl : sink_f) = v;
+        const uint32_t key = f2key(v);
+        const bool hv = valid & (sub0 + jl < oP) & (key > KEY_NEG_INF);
+        atomicAdd(hv ? my_hist + (key >> 21) : sink_h, 1u << (((key >> 20) & 1u) * 16));
+      }
+    };
+    auto epilogue = [&](int i, const f32x4v_t (&ac)[2][HB], float sc) {
+      Epi st;
+#pragma unroll
+      for (int k = 0; k < NPIECE; ++k) piece(k, st, i, ac, sc);
+    };
+    auto convert = [&](const u32x4_t (&src)[NLD], int s) -> bf16x8_t {
+      if constexpr (KST == DT_FP8) {
+        const u32x4_t v = src[s >> 1];
+        const uint32_t w0 = v[(s & 1) * 2], w1 = v[(s & 1) * 2 + 1];
+        u32x4_t o;
+        o[0] = fp8x2_to_bf16x2<false>(w0);
+        o[1] = fp8x2_to_bf16x2<true>(w0);
+        o[2] = fp8x2_to_bf16x2<false>(w1);
+        o[3] = fp8x2_to_bf16x2<true>(w1);
+        return __builtin_bit_cast(bf16x8_t, o);
+      } else {
+        return __builtin_bit_cast(bf16x8_t, src[s]);
+      }
+    };
+
+    constexpr int NM = 2 * HB * NS;                                 // MFMAs per block
+    for (int i0 = 0; i0 < iters; i0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int i = i0 + u;
+        const int x = u & 1;
+        const int up = (u + PF - 1) % PF;                            // slot of block i - 1
+        bf16x8_t bfr[NS];
+        bfr[0] = convert(raw[u], 0);
+        Epi st;
+        __builtin_amdgcn_sched_barrier(0);
+        // MFMAs of block i into set x (t = (s, hb, q), q fastest); between them the conversion
+        // of the next K step, the refill of this slot once converted, and the epilogue of block
+        // i - 1 from set x ^ 1
+#pragma unroll
+        for (int t = 0; t < NM; ++t) {
+          const int s = t / (2 * HB), hb = (t >> 1) % HB, q = t & 1;
+          acc[x][q][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[q][hb][s], bfr[s], s == 0 ? f32x4v_t{} : acc[x][q][hb], 0, 0, 0);
+          if (t % (2 * HB) == 0 && s + 1 < NS) bfr[s + 1] = convert(raw[u], s + 1);
+          if (t == (NS - 2) * 2 * HB) issue_keys(i + PF, raw[u]);
+#pragma unroll
+          for (int k = t * NPIECE / NM; k < (t + 1) * NPIECE / NM; ++k) piece(k, st, i - 1, acc[x ^ 1], scl[up]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        issue_scale(i - 1 + PF, scl[up]);
+      }
+    }
+    epilogue(iters - 1, acc[1], scl[PF - 1]);                      // iters is a multiple of even PF
+    __syncthreads();
+
+    // ---- end of the sub-chunk. Thread t owns first-digit bins [4096 - BPT (t+1), 4096 - BPT t)
+    // of both rows and finds the bin b of each row's k-th largest score in this sub-chunk (both
+    // rows' counts packed in one word: each <= DC_SUB).
+    // The keys in bins >= b are this sub-chunk's candidates.
+    constexpr int BPT = DC_BINS / DC_THREADS;                       // bins per thread
+    static_assert(BPT % 8 == 0, "whole 16-byte reads of packed bins");
+    uint32_t bins[2][BPT];
+    uint32_t part = 0;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      uint32_t sum = 0;
+#pragma unroll
+      for (int c = 0; c < BPT / 8; ++c) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(hist + qq * 2048 + 2048 - (BPT / 2) * (tid + 1) + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bins[qq][8 * c + 2 * e] = w[e] & 0xFFFFu;
+          bins[qq][8 * c + 2 * e + 1] = w[e] >> 16;
+          sum += w[e] & 0xFFFFu;
+          sum += w[e] >> 16;
+        }
+      }
+      part |= sum << (16 * qq);
+    }
+    const uint32_t inc = wave_scan_dpp(part);      // thread order = descending bins
+    if (lane == 63) misc[16 + wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) {
+      before += w < wave ? misc[16 + w] : 0u;
+      total += misc[16 + w];
+    }
+    const uint32_t ex = before + inc - part;
+    const uint32_t k = (uint32_t)a.k;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      if (tid == 0) {
+        misc[4 * qq + 0] = KEY_NEG_INF + 1u;     // every finite score, unless cut below
+        misc[4 * qq + 1] = (total >> (16 * qq)) & 0xFFFFu;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const uint32_t exq = (ex >> (16 * qq)) & 0xFFFFu, sq = (part >> (16 * qq)) & 0xFFFFu;
+      if (exq < k && k <= exq + sq) {
+        uint32_t run = exq;
+#pragma unroll
+        for (int e = BPT - 1; e >= 0; --e) {
+          if (run + bins[qq][e] >= k) {
+            misc[4 * qq + 0] = (uint32_t)(DC_BINS - BPT * (tid + 1) + e) << 20;
+            misc[4 * qq + 1] = run + bins[qq][e];
+            break;
+          }
+          run += bins[qq][e];
+        }
+      }
+    }
+    __syncthreads();
+    // the candidates of a sub-chunk go to the same slots of the row's candidate list (a key is a
+    // candidate of one sub-chunk only), and their count to the sub-chunk's counter
+    if (tid < nrows) a.ccount[(tid ? r1 : r0) * a.nsegs + sub0 / a.sub] = misc[4 * tid + 1];
+    // ---- candidates (order-preserving key, slot) at or above each row's bound. Wave w takes
+    // the slots j with (j / 256) % DC_WAVES == w, 4 per lane per step: a first pass counts them
+    // (ballots), the waves' counts are prefix-summed, a second pass writes them.
+    const int len = sub1 - sub0;
+    const int steps = (len + 4 * DC_THREADS - 1) / (4 * DC_THREADS);
+    auto sel_masks = [&](int qq, int st, uint32_t thr, uint32_t (&key)[4], uint64_t (&m)[4]) {
+      const int j0 = st * 4 * DC_THREADS + wave * 256 + 4 * lane;
+      const int jr = min(j0, a.sub - 4);
+      const int lim = min(len, (qq ? P1 : P0) - sub0);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ssc + qq * a.sub + jr);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[e] = f2key(v[e]);
+        m[e] = __ballot(j0 + e < lim && key[e] >= thr);
+      }
+    };
+    uint32_t wcnt[2] = {0u, 0u};
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      if (qq < nrows) {
+        const uint32_t thr = misc[4 * qq];
+        for (int st = 0; st < steps; ++st) {
+          uint32_t key[4];
+          uint64_t m[4];
+          sel_masks(qq, st, thr, key, m);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wcnt[qq] += (uint32_t)__popcll(m[e]);
+        }
+      }
+    }
+    if (lane == 0) {
+      misc[16 + wave] = wcnt[0];
+      misc[24 + wave] = wcnt[1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      if (qq < nrows) {
+        const uint32_t thr = misc[4 * qq];
+        uint32_t pos = (uint32_t)sub0;
+        for (int w = 0; w < wave; ++w) pos += misc[16 + 8 * qq + w];
+        const int64_t rr = qq ? r1 : r0;
+        uint32_t* ck = a.cand_key + rr * a.cand_cap;
+        uint32_t* ci = a.cand_idx + rr * a.cand_cap;
+        for (int st = 0; st < steps; ++st) {
+          uint32_t key[4];
+          uint64_t m[4];
+          sel_masks(qq, st, thr, key, m);
+          const uint32_t jb = (uint32_t)(sub0 + st * 4 * DC_THREADS + wave * 256 + 4 * lane);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], 0u));
+            if ((m[e] >> lane) & 1u) {
+              ck[pos + below] = key[e];
+              ci[pos + below] = jb + e;
+            }
+            pos += (uint32_t)__popcll(m[e]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Bin of the need-th largest element of a 4096-bin histogram in LDS, by all RS_THREADS threads
+// (thread t holds the 8 bins below 4096 - 8 t): out = {bin or ~0u if need exceeds the total, count
+// in higher bins}. sh: RS_WAVES words of scratch.
+constexpr int RS_THREADS = 512;
+constexpr int RS_WAVES = RS_THREADS / 64;
+constexpr int RS_LDS_CAND = 4096;
+
+__device__ __forceinline__ void block_find_desc(const uint32_t* h, uint32_t need, uint32_t* sh, uint32_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lo = DC_BINS - 8 * (tid + 1);                 // bins [lo, lo + 8)
+  const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(h + lo);
+  const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(h + lo + 4);
+  const uint32_t c[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sum += c[e];
+  const uint32_t inc = wave_scan_dpp(sum);
+  if (lane == 63) sh[wave] = inc;
+  if (tid == 0) {
+    out[0] = ~0u;
+    out[1] = 0u;
+  }
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < RS_WAVES; ++w) before += w < wave ? sh[w] : 0u;
+  const uint32_t ex = before + inc - sum;                 // count in higher bins than mine
+  if (ex < need && need <= ex + sum) {
+    uint32_t run = ex;
+#pragma unroll
+    for (int e = 7; e >= 0; --e) {
+      if (run + c[e] >= need) {
+        out[0] = (uint32_t)(lo + e);
+        out[1] = run;
+        break;
+      }
+      run += c[e];
+    }
+  }
+  __syncthreads();
+}
+
+// One work-group per row. The row's candidates (per sub-chunk lists written by the scan) hold
+// every key the selection can take, and at least min(k, finite slots) keys, so the selection
+// is the top min(k, M) of the M candidates: the 12-bit bin b1 of the k-th largest from their
+// histogram, candidates above b1 written out, the ones in b1 resolved exactly with two more
+// 10-bit digits and, for ties at the k-th key, three digits of the complemented slot (lowest
+// slots first); then the padding.
+
+__global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a) {
+  __shared__ __align__(16) uint32_t hist[DC_BINS];
+  __shared__ uint32_t ckey[RS_LDS_CAND];
+  __shared__ uint32_t cpos[RS_LDS_CAND];
+  __shared__ uint32_t sh[RS_WAVES];
+  __shared__ uint32_t bc[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const uint32_t* counts = a.ccount + r * a.nsegs;
+  const uint32_t* gk = a.cand_key + r * a.cand_cap;
+  const uint32_t* gi = a.cand_idx + r * a.cand_cap;
+  uint32_t* g2k = a.cand2_key + r * a.cand_cap;
+  uint32_t* g2p = a.cand2_idx + r * a.cand_cap;
+  int32_t* oidx = a.out_idx + r * a.k;
+  float* osc = a.out_score ? a.out_score + r * a.k : nullptr;
+
+  // ---- candidate count M
+  uint32_t M = 0;
+  {
+    uint32_t part = 0;
+    for (int sg = tid; sg < a.nsegs; sg += RS_THREADS) part += counts[sg];
+    const uint32_t inc = wave_scan_dpp(part);
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) M += sh[w];
+    __syncthreads();
+  }
+  const uint32_t kk = min((uint32_t)a.k, M);
+  const bool all = kk == M;
+
+  for (int i = tid; i < DC_BINS; i += RS_THREADS) hist[i] = 0u;
+  if (tid == 0) {
+    bc[4] = 0u;                                  // written
+    bc[5] = 0u;                                  // bin-b1 candidates
+  }
+  __syncthreads();
+
+  // visits every candidate (key, position in the list), 4 loads per thread in flight
+  auto for_each = [&](auto f) {
+    for (int sg = 0; sg < a.nsegs; ++sg) {
+      const int c = (int)counts[sg];
+      const uint32_t base = (uint32_t)sg * (uint32_t)a.sub;
+      for (int j0 = 0; j0 < c; j0 += 4 * RS_THREADS) {
+        uint32_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = gk[base + min(j0 + u * RS_THREADS + tid, c - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) f(j0 + u * RS_THREADS + tid < c, x[u], base + j0 + u * RS_THREADS + tid);
+      }
+    }
+  };
+
+  // ---- pass 1: first-digit histogram, bin b1 of the kk-th largest
+  if (!all) {
+    for_each([&](bool ok, uint32_t x, uint32_t) {
+      if (ok) atomicAdd(&hist[x >> 20], 1u);
+    });
+  }
+  __syncthreads();
+  uint32_t b1 = 0, above = 0;
+  if (!all) {
+    block_find_desc(hist, kk, sh, bc);
+    b1 = bc[0];
+    above = bc[1];
+  }
+
+  // ---- pass 2: candidates above b1 out (all when every candidate is selected), bin b1 kept
+  // as (key, position in the list)
+  if (kk > 0) {
+    for_each([&](bool ok, uint32_t x, uint32_t p) {
+      const bool sel = ok && (all || (x >> 20) > b1);
+      const bool cand = ok && !all && (x >> 20) == b1;
+      const uint64_t ms = __ballot(sel), mc = __ballot(cand);
+      uint32_t ps = 0, pc = 0;
+      if (lane == 0) {
+        if (ms) ps = atomicAdd(&bc[4], (uint32_t)__popcll(ms));
+        if (mc) pc = atomicAdd(&bc[5], (uint32_t)__popcll(mc));
+      }
+      const uint32_t bs = __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
+      const uint32_t bcn = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
+      if (sel) {
+        const uint32_t pos = wave_bcast(ps, 0) + bs;
+        oidx[pos] = (int32_t)gi[p];
+        if (osc) osc[pos] = key2f(x);
+      }
+      if (cand) {
+        const uint32_t cp = wave_bcast(pc, 0) + bcn;
+        if (cp < (uint32_t)RS_LDS_CAND) {
+          ckey[cp] = x;
+          cpos[cp] = p;
+        } else {
+          g2k[cp] = x;
+          g2p[cp] = p;
+        }
+      }
+    });
+  }
+  __syncthreads();
+
+  if (kk > 0 && !all) {
+    const uint32_t nc = bc[5];
+    // slots of the bin-b1 candidates (their list positions are replaced by the slots)
+    for (uint32_t j = tid; j < nc; j += RS_THREADS) {
+      if (j < (uint32_t)RS_LDS_CAND) cpos[j] = gi[cpos[j]];
+      else g2p[j] = gi[g2p[j]];
+    }
+    __syncthreads();
+    auto get = [&](uint32_t j, uint32_t& x, uint32_t& i) {
+      if (j < (uint32_t)RS_LDS_CAND) {
+        x = ckey[j];
+        i = cpos[j];
+      } else {
+        x = g2k[j];
+        i = g2p[j];
+      }
+    };
+    // one radix pass over the bin-b1 candidates: histogram of digit(x, i) over the matching
+    // ones, then the bin holding the need-th largest; out = {bin, count above it, count in it}
+    auto pass = [&](auto match, auto digit, int nb, uint32_t need, uint32_t* out) {
+      __syncthreads();
+      for (int q = tid; q < nb; q += RS_THREADS) hist[q] = 0u;
+      __syncthreads();
+      for (uint32_t j = tid; j < nc; j += RS_THREADS) {
+        uint32_t x, i;
+        get(j, x, i);
+        if (match(x, i)) atomicAdd(&hist[digit(x, i)], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        int bn;
+        uint32_t ab;
+        wave_hist_find(hist, nb, need, &bn, &ab);
+        if (lane == 0) {
+          bc[0] = (uint32_t)max(bn, 0);
+          bc[1] = ab;
+          bc[2] = bn >= 0 ? hist[bn] : 0u;
+        }
+      }
+      __syncthreads();
+      out[0] = bc[0];
+      out[1] = bc[1];
+      out[2] = bc[2];
+    };
+    uint32_t need = kk - above;
+    uint32_t rr[3];
+    pass([&](uint32_t, uint32_t) { return true; },
+         [&](uint32_t x, uint32_t) { return (x >> 10) & 0x3FFu; }, 1024, need, rr);
+    const uint32_t pre2 = (b1 << 10) | rr[0];
+    need -= rr[1];
+    pass([&](uint32_t x, uint32_t) { return (x >> 10) == pre2; },
+         [&](uint32_t x, uint32_t) { return x & 0x3FFu; }, 1024, need, rr);
+    const uint32_t T = (pre2 << 10) | rr[0];
+    const uint32_t need_eq = need - rr[1], n_eq = rr[2];
+    uint32_t CI = 0u;                         // ties kept: complemented slot >= CI
+    if (n_eq != need_eq) {
+      pass([&](uint32_t x, uint32_t) { return x == T; },
+           [&](uint32_t, uint32_t i) { return (~i) >> 21; }, 2048, need_eq, rr);
+      const uint32_t d4 = rr[0];
+      uint32_t ne = need_eq - rr[1];
+      pass([&](uint32_t x, uint32_t i) { return x == T && ((~i) >> 21) == d4; },
+           [&](uint32_t, uint32_t i) { return ((~i) >> 10) & 0x7FFu; }, 2048, ne, rr);
+      const uint32_t d5 = (d4 << 11) | rr[0];
+      ne -= rr[1];
+      pass([&](uint32_t x, uint32_t i) { return x == T && ((~i) >> 10) == d5; },
+           [&](uint32_t, uint32_t i) { return (~i) & 0x3FFu; }, 1024, ne, rr);
+      CI = (d5 << 10) | rr[0];
+    }
+    // the rest follow the candidates above b1
+    for (uint32_t j0 = 0; j0 < nc; j0 += RS_THREADS) {
+      const uint32_t j = j0 + tid;
+      bool sel = false;
+      uint32_t x = 0, i = 0;
+      if (j < nc) {
+        get(j, x, i);
+        sel = x > T || (x == T && ~i >= CI);
+      }
+      const uint64_t m = __ballot(sel);
+      uint32_t pb = 0;
+      if (lane == 0 && m) pb = atomicAdd(&bc[4], (uint32_t)__popcll(m));
+      pb = wave_bcast(pb, 0);
+      if (sel) {
+        const uint32_t pos = pb + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        oidx[pos] = (int32_t)i;
+        if (osc) osc[pos] = key2f(x);
+      }
+    }
+  }
+  for (int p = (int)kk + tid; p < a.k; p += RS_THREADS) {
+    oidx[p] = -1;
+    if (osc) osc[p] = -INFINITY;
+  }
+}
+
+bool decode_supported(int q_dtype, int k_dtype, int H, int D, int T, int N) {
+  // 32-bit byte offsets within one sequence's keys
+  const int64_t seq_bytes = (int64_t)N * D * (k_dtype == DT_FP8 ? 1 : 2);
+  return q_dtype == DT_BF16 && (k_dtype == DT_FP8 || k_dtype == DT_BF16) && H <= 64 &&
+         (D == 64 || D == 128) && T <= 4 && N >= 2048 && seq_bytes < (int64_t(1) << 31);
+}
+
+size_t decode_scan_lds(int sub) { return (size_t)8 * sub + 2 * 2048 * 4 + (32 + 128) * 4; }
+
+template <int D, int HB, int KST>
+static hipError_t launch_scan(const DecodeArgs& a, hipStream_t s) {
+  auto kfn = decode_scan_kernel<D, HB, KST, dc_pf<KST>()>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)decode_scan_lds(DC_SUB));
+  if (e != hipSuccess) return e;
+  dim3 grid(a.B * a.nchunk, (a.T + 1) / 2);
+  hipLaunchKernelGGL(kfn, grid, dim3(DC_THREADS), decode_scan_lds(a.sub), s, a);
+  return hipGetLastError();
+}
+
+template <int D, int KST>
+static hipError_t launch_scan_h(const DecodeArgs& a, hipStream_t s) {
+  const int hb = (a.H + 15) / 16;
+  if (hb == 1) return launch_scan<D, 1, KST>(a, s);
+  if (hb == 2) return launch_scan<D, 2, KST>(a, s);
+  return launch_scan<D, 4, KST>(a, s);
+}
+
+hipError_t launch_decode_scan(const DecodeArgs& a, hipStream_t s) {
+  if (a.sub < DC_KB || a.sub > DC_SUB || a.sub % 64) return hipErrorInvalidValue;
+  if (a.k_dtype == DT_FP8)
+    return a.D == 128 ? launch_scan_h<128, DT_FP8>(a, s) : launch_scan_h<64, DT_FP8>(a, s);
+  return a.D == 128 ? launch_scan_h<128, DT_BF16>(a, s) : launch_scan_h<64, DT_BF16>(a, s);
+}
+
+hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(decode_select_kernel, dim3(a.B * a.T), dim3(RS_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace idx

@@ -84,6 +84,26 @@ struct BlockRefineArgs {
   int32_t* row_meta; int topk_k;
 };
 
+// Decode scan + selection (few queries per sequence, long cache): see decode.hip.
+constexpr int DECODE_BINS = 4096;  // first-digit histogram bins per row
+constexpr int DECODE_SUB = 16384;  // keys per scan sub-chunk (scores held in LDS)
+struct DecodeArgs {
+  const void* q; const float* w; const int32_t* q_pos;      // bf16 [B, T, H, D], [B, T, H], [B, T]
+  const void* keys; int k_dtype; const float* k_scale;      // [B, N, D] FP8 or bf16, [B, N]
+  const int32_t* k_len;
+  int B, T, H, D, N;
+  int nchunk, chunk, sub;          // key chunks per sequence (scan work-groups), keys per chunk,
+                                   // keys per sub-chunk (multiple of 64, at most DECODE_SUB,
+                                   // dividing chunk)
+  uint32_t* ccount;                // [B*T][nsegs] candidates per sub-chunk (written by the scan)
+  int nsegs;                       // sub-chunks per row: ceil(N / sub)
+  uint32_t* cand_key; uint32_t* cand_idx;                    // [B*T][cand_cap] scan candidates
+  uint32_t* cand2_key; uint32_t* cand2_idx;                  // [B*T][cand_cap] bin-b1 candidates
+  int cand_cap;                    // >= N, multiple of 64
+  int k;                           // selection size
+  int32_t* out_idx; float* out_score;                        // [B, T, k]
+};
+
 hipError_t launch_score(const ScoreArgs& a, int n_splits, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
@@ -92,6 +112,9 @@ hipError_t launch_block_refine(const BlockRefineArgs& a, hipStream_t s);
 hipError_t launch_sort_rows(int32_t* rows, int stride, const int32_t* count, int n_rows, int max_count,
                             hipStream_t s);
 bool score_supported(int q_dtype, int k_dtype, int H, int D);
+bool decode_supported(int q_dtype, int k_dtype, int H, int D, int T, int N);
+hipError_t launch_decode_scan(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t s);
 
 constexpr int KEY_TILE = 64;       // keys per LDS tile of the score kernels
 constexpr int Q_TILE = 8;          // queries per work-group tile (one per wave)
