@@ -1,6 +1,8 @@
 """Benchmark of the MI355X DSA lightning indexer.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense16k] [--no-cpu]
+    python bench.py --copy-probe BYTES     (a plain device copy of known size, for calibrating
+                                            the HBM byte counters of rocprofv3 --pmc)
 
 One step = one full indexer call (every stage of the path: scoring, masking, top-k selection,
 and for the variants the proxy / pooling / candidate stages) over one batch of seeded synthetic
@@ -12,7 +14,9 @@ dense-equivalent count) divided by the mean step time. Top-k rows per second are
 beside it. roofline = the dominant kernel's algorithmic flops (or HBM bytes) per launch over its
 mean launch duration, timed with HIP events recorded by the library on the launch stream.
 cpu_baseline = the CPU oracle (float64 numpy) timed on a bounded row sample of the same
-workload on this host.
+workload on this host. roofline.traffic = the dominant kernel's HBM bytes per launch from the
+FETCH_SIZE / WRITE_SIZE counters recorded in profiles/traffic.json, each scaled by what the same
+counter reads for a plain copy of known size; null when the kernel sources changed since.
 """
 from __future__ import annotations
 
@@ -32,6 +36,47 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def csrc_digest():
+    """sha256 over the kernel sources and build flags (changes whenever a kernel may change)."""
+    import hashlib
+    pkg = os.path.join(ROOT, "sparse_attention_indexer_02_amd")
+    h = hashlib.sha256()
+    files = sorted(os.path.join(pkg, "csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))
+                   if f.endswith((".hip", ".h")))
+    for f in files + [os.path.join(pkg, "build.py")]:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/traffic.json, or None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+        e = d["kernels"][f"{kernel}@{workload}"]
+        if e["csrc_sha256"] != csrc_digest():
+            return None
+        c = d["copy"]
+        rf = c["bytes"] / (c["fetch_kib"] * 1024.0)
+        wf = c["bytes"] / (c["write_kib"] * 1024.0)
+        return e["fetch_kib"] * 1024.0 * rf + e["write_kib"] * 1024.0 * wf
+    except (OSError, KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+def copy_probe(nbytes):
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": (nbytes // 4) * 4, "launches": 5}))
 
 
 # ----------------------------------------------------------------------------------------------
@@ -138,11 +183,15 @@ def main():
     ap.add_argument("--workload", default="dense16k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the indexer here is "
               "single-GPU by design", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import numpy as np
     import torch
@@ -221,8 +270,8 @@ def main():
         achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": None, "per_launch": f"{flops / (n / args.steps):.4g} flop",
-                "mean_launch_ms": ms / n}
+                "traffic": measured_traffic(args.workload, "score_kernel"),
+                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
     elif op == "dense":
         # decode shape: the streaming scan is the dominant kernel, bound by the key-cache read
         ms, n = kernels["decode_scan"]
@@ -230,7 +279,8 @@ def main():
         achieved = byts / (n / args.steps) / (ms / n * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "decode_scan_kernel", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "traffic": None, "per_launch": f"{byts / (n / args.steps):.4g} B",
+                "traffic": measured_traffic(args.workload, "decode_scan_kernel"),
+                "per_launch": f"{byts / (n / args.steps):.4g} B",
                 "mean_launch_ms": ms / n}
     elif op == "group":
         pp, rp = group_refine_pairs(prob, spec["group_size"], spec["n_cand"])
@@ -239,8 +289,8 @@ def main():
         achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": None, "per_launch": f"{flops / (n / args.steps):.4g} flop",
-                "mean_launch_ms": ms / n}
+                "traffic": measured_traffic(args.workload, "score_kernel"),
+                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
         cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"],
                    algorithmic_pairs_per_step=pp + rp)
     else:
@@ -250,8 +300,8 @@ def main():
         achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "block_refine_kernel", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": None, "per_launch": f"{flops / (n / args.steps):.4g} flop",
-                "mean_launch_ms": ms / n}
+                "traffic": measured_traffic(args.workload, "block_refine_kernel"),
+                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
         cfg.update(block_size=spec["block_size"], n_blocks_keep=spec["n_blocks_keep"],
                    algorithmic_pairs_per_step=cp + rp)
     cfg["kernel_ms_per_step"] = {n_: round(ms_ / args.steps, 4) for n_, (ms_, c) in kernels.items() if c}
