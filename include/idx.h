@@ -68,7 +68,9 @@ enum { IDX_OP_SCORE_TOPK = 0, IDX_OP_GROUP = 1, IDX_OP_BLOCK = 2 };
  *                         q_pos < 0 means an empty prefix
  *   k_len   [B] int32     keys present in each sequence's cache, or NULL for N
  * Built shapes: H in 1..128, D in {32, 64, 128}. Prefill (T large) and decode (T = 1..4 multi-token
- * prediction queries against a long cache) use the same call. */
+ * prediction queries against a long cache) use the same call; decode-shaped problems (bf16
+ * queries, FP8 or bf16 keys, H <= 64, D in {64, 128}, T <= 4, N >= 2048) take a streaming path
+ * whose workspace differs, so size it with idx_workspace_bytes for the same shape. */
 typedef struct idx_problem {
   int32_t B, T, H, D, N;
   int32_t q_dtype, k_dtype;
@@ -132,7 +134,8 @@ const char* idx_strerror(int status);
  * records a HIP event pair around each kernel launch on the call's stream. idx_timer_read
  * waits for the recorded events and returns the summed milliseconds and the launch count of
  * the kernels whose name contains `kernel_substr` (all kernels if NULL or ""); kernel names are
- * "score", "topk", "proxy", "pool" and "block_refine". idx_timer_enable(on) clears the record
+ * "score", "topk", "sort", "proxy", "pool", "block_refine", "decode_scan" and "decode_select".
+ * idx_timer_enable(on) clears the record
  * and switches recording on or off. Not thread safe. */
 int idx_timer_enable(int on);
 int idx_timer_read(const char* kernel_substr, double* total_ms, int32_t* launches);
