@@ -386,7 +386,7 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
   }
   // candidate lists in ascending token order (the refine indexes them by slot)
   if ((st = from_hip(timed("sort", s, [&] {
-         return launch_sort_rows(pl.cand, C, pl.cand_cnt, p->B * pl.NG, C, s);
+         return launch_sort_rows(pl.cand, C, pl.cand_cnt, p->B * pl.NG, C, p->N, s);
        }))))
     return st;
   // per-member refine over the group's candidates
@@ -451,7 +451,7 @@ int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_
     if ((st = from_hip(run_topk(t, pl.NB, s)))) return st;
   }
   if ((st = from_hip(timed("sort", s, [&] {
-         return launch_sort_rows(pl.blocks, keep, pl.n_kept, p->B * p->T, keep, s);
+         return launch_sort_rows(pl.blocks, keep, pl.n_kept, p->B * p->T, keep, pl.NB, s);
        }))))
     return st;
   // token refine inside the kept blocks

@@ -109,8 +109,9 @@ hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_block_refine(const BlockRefineArgs& a, hipStream_t s);
+// Sorts rows of distinct values in [0, max_value) ascending (count[r] values in row r).
 hipError_t launch_sort_rows(int32_t* rows, int stride, const int32_t* count, int n_rows, int max_count,
-                            hipStream_t s);
+                            int max_value, hipStream_t s);
 bool score_supported(int q_dtype, int k_dtype, int H, int D);
 bool decode_supported(int q_dtype, int k_dtype, int H, int D, int T, int N);
 hipError_t launch_decode_scan(const DecodeArgs& a, hipStream_t s);

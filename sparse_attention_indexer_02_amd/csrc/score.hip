@@ -260,7 +260,7 @@ score_kernel(ScoreArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (fuse && active) {
     int bin;

@@ -149,6 +149,14 @@ struct DirectLoader {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Work-group barrier for reusing LDS tiles: waits for this wave's LDS operations only, then
+// s_barrier. Unlike __syncthreads() it does not first wait for the wave's global stores (the
+// score rows) to complete, which would put a store round trip on every tile.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+}
+
 // ReLU through an integer max: an IEEE float is negative iff its bit pattern is negative as an
 // int32, so max(bits, 0) is bits(x) for x >= +0 and +0 otherwise (one VALU op, no NaN quieting).
 __device__ __forceinline__ float relu(float x) {

@@ -692,9 +692,56 @@ __global__ void __launch_bounds__(256) sort_rows_kernel(int32_t* rows, int strid
   for (int i = threadIdx.x; i < c; i += blockDim.x) row[i] = sv[i];
 }
 
+// Ascending order of rows of DISTINCT values in [0, max_value): the values become bits of an LDS
+// bitmap, and each thread writes the set bits of its contiguous range of words at its exclusive
+// prefix of the popcounts. One pass over the row and one over the bitmap.
+__global__ void __launch_bounds__(256) sort_rows_bitmap_kernel(int32_t* rows, int stride, const int32_t* count,
+                                                               int nwords) {
+  extern __shared__ uint32_t bm[];
+  __shared__ uint32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x;
+  int32_t* row = rows + (int64_t)r * stride;
+  const int c = count[r];
+  for (int i = tid; i < nwords; i += 256) bm[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < c; i += 256) {
+    const uint32_t v = (uint32_t)row[i];
+    atomicOr(&bm[v >> 5], 1u << (v & 31u));
+  }
+  __syncthreads();
+  const int per = (nwords + 255) / 256;
+  const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+  const uint32_t inc = wave_scan_dpp(cnt);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t pos = inc - cnt;
+  for (int w = 0; w < wave; ++w) pos += wsum[w];
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = bm[w];
+    while (m) {
+      row[pos++] = w * 32 + __builtin_ctz(m);
+      m &= m - 1u;
+    }
+  }
+}
+
 hipError_t launch_sort_rows(int32_t* rows, int stride, const int32_t* count, int n_rows, int max_count,
-                            hipStream_t s) {
+                            int max_value, hipStream_t s) {
   if (n_rows <= 0 || max_count <= 1) return hipSuccess;
+  const int nwords = (max_value + 31) / 32;
+  if (max_value > 0 && nwords <= 32768) {
+    const size_t lds = (size_t)nwords * sizeof(uint32_t);
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sort_rows_bitmap_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sort_rows_bitmap_kernel, dim3(n_rows), dim3(256), lds, s, rows, stride, count, nwords);
+    return hipGetLastError();
+  }
   int pow2 = 1;
   while (pow2 < max_count) pow2 <<= 1;
   const size_t lds = (size_t)pow2 * sizeof(int32_t);
