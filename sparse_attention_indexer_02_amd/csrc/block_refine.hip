@@ -180,6 +180,225 @@ block_refine_kernel(BlockRefineArgs a) {
   }
 }
 
+// bf16 keys and queries: the union's key rows stream straight into LDS (global_load_lds, 128-key
+// tiles, double-buffered) and a wave that owns all four 32-key steps of a tile runs them
+// pipelined (the epilogue of one step under the MFMAs of the next, the next step's fragments read
+// during the current step), as the dense score kernel does; partly owned tiles run step by step.
+template <int D, int HB>
+__global__ void __launch_bounds__(WavesFor<HB>::value * 64)
+block_refine_direct_kernel(BlockRefineArgs a) {
+  constexpr int NW = WavesFor<HB>::value;
+  constexpr int NTHR = NW * 64;
+  constexpr int KT = 128;
+  constexpr int NSUB = KT / 32;
+  typedef Geo<MmaBf16, D, KT> G;
+  typedef DirectLoader<D, NTHR, KT> DLoader;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* tiles = smem;
+  int16_t* pos_tab = reinterpret_cast<int16_t*>(smem + 2 * G::TILE_BYTES);   // [NW][UMAX]
+  int32_t* ublk = reinterpret_cast<int32_t*>(pos_tab + NW * BR_UMAX);        // [UMAX]
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(ublk + BR_UMAX);            // [NBW]
+  uint32_t* wpre = bitmap + BR_NBW;                                          // [NBW]
+  uint32_t* sh = wpre + BR_NBW;                                              // [80]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lin = gridDim.x - 1 - blockIdx.x;
+  const int b = lin % a.B;
+  const int ti = lin / a.B;
+  const int tb = a.t0 + ti * NW, te = min(tb + NW, a.t1);
+  const int t = tb + wave;
+  const bool active = t < te;
+  const int kl = a.k_len ? max(0, min(a.k_len[b], a.N)) : a.N;
+  const int Bs = a.block_size;                      // a power of two here
+  const int lb = __builtin_ctz((unsigned)Bs);
+  const int NB = (kl + Bs - 1) >> lb;
+  const int NBW = (NB + 31) / 32;
+  const int64_t qrow_i = (int64_t)b * a.T + (active ? t : tb);
+  const int my_pos = active ? a.q_pos[qrow_i] : -1;
+  const int nk = active ? a.n_kept[qrow_i] : 0;
+  const int32_t* mylist = a.blocks + qrow_i * a.keep_stride;
+  if (active && lane == 0) a.row_len[(int64_t)b * a.rows_per_seq + (t - a.t0)] = nk * Bs;
+
+  // union of the tile's kept blocks
+  for (int i = tid; i < NBW; i += NTHR) bitmap[i] = 0u;
+  __syncthreads();
+  for (int p = lane; p < nk; p += 64) {
+    const int blk = mylist[p];
+    atomicOr(&bitmap[blk >> 5], 1u << (blk & 31));
+  }
+  __syncthreads();
+  uint32_t n_union;
+  {
+    const int per = (NBW + NTHR - 1) / NTHR;
+    const int w0 = tid * per;
+    uint32_t c = 0;
+    for (int i = 0; i < per; ++i)
+      if (w0 + i < NBW) c += __popc(bitmap[w0 + i]);
+    const uint32_t inc = wave_incl_scan(c);
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t s = lane < NW ? sh[lane] : 0u;
+      const uint32_t si = wave_incl_scan(s);
+      if (lane < NW) sh[32 + lane] = si - s;
+      if (lane == 63) sh[64] = si;
+    }
+    __syncthreads();
+    uint32_t run = sh[32 + wave] + inc - c;
+    for (int i = 0; i < per; ++i)
+      if (w0 + i < NBW) {
+        wpre[w0 + i] = run;
+        run += __popc(bitmap[w0 + i]);
+      }
+    n_union = sh[64];
+    __syncthreads();
+  }
+
+  bf16x8_t qf[HB][G::NKK];
+  float wv[HB][16];
+  {
+    const int hh = lane >> 5, ln = lane & 31;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int head = 32 * hb + ln;
+      const bool ok = active && head < a.H;
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + (qrow_i * a.H + (ok ? head : 0)) * D * 2;
+#pragma unroll
+      for (int kk = 0; kk < G::NKK; ++kk)
+        qf[hb][kk] = ok ? load_frag<MmaBf16>(qrow, DT_BF16, hh * (D / 2) + kk * 8) : bf16x8_t{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int h = acc_head(hb, r, lane);
+        wv[hb][r] = (active && h < a.H) ? a.w[qrow_i * a.H + h] : 0.f;
+      }
+    }
+  }
+
+  const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)b * a.N * (D * 2);
+  float* srow = a.scores + ((int64_t)b * a.rows_per_seq + (active ? t - a.t0 : 0)) * a.score_stride;
+
+  for (uint32_t rb = 0; rb < n_union; rb += BR_UMAX) {
+    const int rcount = (int)min((uint32_t)BR_UMAX, n_union - rb);
+    {
+      const int per = (NBW + NTHR - 1) / NTHR;
+      const int w0 = tid * per;
+      for (int i = 0; i < per; ++i) {
+        const int wi = w0 + i;
+        if (wi >= NBW) break;
+        uint32_t m = bitmap[wi];
+        uint32_t u = wpre[wi];
+        while (m) {
+          const int bit = __builtin_ctz(m);
+          m &= m - 1;
+          if (u >= rb && u < rb + (uint32_t)rcount) ublk[u - rb] = wi * 32 + bit;
+          ++u;
+        }
+      }
+      for (int i = tid; i < NW * rcount; i += NTHR) pos_tab[(i / rcount) * BR_UMAX + i % rcount] = -1;
+    }
+    __syncthreads();
+    for (int p = lane; p < nk; p += 64) {
+      const int blk = mylist[p];
+      const uint32_t u = wpre[blk >> 5] + __popc(bitmap[blk >> 5] & ((1u << (blk & 31)) - 1u));
+      if (u >= rb && u < rb + (uint32_t)rcount) pos_tab[wave * BR_UMAX + (u - rb)] = (int16_t)p;
+    }
+    __syncthreads();
+
+    const int nslots = rcount * Bs;
+    auto key_at = [&](int v) -> int {                // key of union slot v, or -1
+      if (v >= nslots) return -1;
+      const int key = (ublk[v >> lb] << lb) + (v & (Bs - 1));
+      return key < kl ? key : -1;
+    };
+    const int ntile = (nslots + KT - 1) / KT;
+    int kidx[DLoader::ITERS];
+    auto fetch_idx = [&](int base) {
+#pragma unroll
+      for (int i = 0; i < DLoader::ITERS; ++i) kidx[i] = key_at(base + DLoader::row_of(i, wave, lane));
+    };
+    fetch_idx(0);
+    DLoader::load_idx(kseq, tiles, wave, lane, kidx);
+    if (ntile > 1) fetch_idx(KT);
+    wait_vmem();
+    __syncthreads();
+    bf16x8_t bfr[G::NKK];
+    for (int it = 0; it < ntile; ++it) {
+      const int cur = it & 1;
+      const int base = it * KT;
+      const bool more = it + 1 < ntile;
+      if (more) {
+        DLoader::load_idx(kseq, tiles + (cur ^ 1) * G::TILE_BYTES, wave, lane, kidx);
+        if (it + 2 < ntile) fetch_idx(base + 2 * KT);
+      }
+      const uint8_t* tile = tiles + cur * G::TILE_BYTES;
+      // kept position of a union slot's block for this wave's query, or -1
+      auto kept_pos = [&](int v) -> int { return v < nslots ? pos_tab[wave * BR_UMAX + (v >> lb)] : -1; };
+      // steps holding at least one of the query's blocks (lanes l and l + 32 share key l % 32)
+      uint32_t own = 0;
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+        if (__ballot(kept_pos(base + s * 32 + (lane & 31)) >= 0) != 0ull) own |= 1u << s;
+      if (!active) own = 0;
+      // scores, two steps per value: lanes 0-31 hold the even step, lanes 32-63 the odd one
+      float ov[NSUB / 2];
+#pragma unroll
+      for (int p = 0; p < NSUB / 2; ++p) ov[p] = 0.f;
+      auto put = [&](int st, float tot) {
+        if ((st & 1) == (lane >> 5)) ov[st >> 1] = tot;
+      };
+      if (own == (1u << NSUB) - 1u) {
+        f32x16_t A[HB], Bq[HB];
+        load_bfrag<D, KT>(tile, 0, lane, bfr);
+        tile_mma_rot<D, HB, KT>(qf, bfr, tile, 32, true, lane, A);
+#pragma unroll
+        for (int s = 1; s < NSUB; ++s) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (s & 1) {
+            tile_mma_rot<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, lane, Bq);
+            put(s - 1, tile_epilogue<HB>(A, wv));
+          } else {
+            tile_mma_rot<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, lane, A);
+            put(s - 1, tile_epilogue<HB>(Bq, wv));
+          }
+#pragma unroll
+          for (int kk = 0; kk < G::NKK; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, HB, 0);
+            if (s + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (16 * HB * 2 + 8) / G::NKK + 1, 0);
+          }
+        }
+        put(NSUB - 1, tile_epilogue<HB>(Bq, wv));
+      } else {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          if (own & (1u << s)) {
+            f32x16_t acc[HB];
+            load_bfrag<D, KT>(tile, s * 32, lane, bfr);
+            tile_mma_rot<D, HB, KT>(qf, bfr, tile, 0, false, lane, acc);
+            put(s, tile_epilogue<HB>(acc, wv));
+          }
+        }
+      }
+      if (more) wait_vmem();
+      // lanes 0-31 store the even steps, lanes 32-63 the odd ones
+#pragma unroll
+      for (int p = 0; p < NSUB / 2; ++p) {
+        const int s = 2 * p + (lane >> 5);
+        const int slot = base + s * 32 + (lane & 31);
+        const int m = kept_pos(slot);
+        const float v = ov[p];
+        if (m >= 0) {
+          const int o = slot & (Bs - 1);
+          const int key = (ublk[slot >> lb] << lb) + o;
+          srow[(m << lb) + o] = (key < kl && key <= my_pos) ? v : -INFINITY;
+        }
+      }
+      lds_barrier();
+    }
+  }
+}
+
 template <class Mma, int D, int HB, int KST>
 static hipError_t launch_br(const BlockRefineArgs& a, hipStream_t s) {
   constexpr int NW = WavesFor<HB>::value;
@@ -208,8 +427,28 @@ static hipError_t launch_br_dh(const BlockRefineArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int D, int HB>
+static hipError_t launch_brd(const BlockRefineArgs& a, hipStream_t s) {
+  constexpr int NW = WavesFor<HB>::value;
+  typedef Geo<MmaBf16, D, 128> G;
+  const size_t lds = 2 * G::TILE_BYTES + NW * BR_UMAX * sizeof(int16_t) +
+                     BR_UMAX * sizeof(int32_t) + 2 * BR_NBW * sizeof(uint32_t) + 80 * sizeof(uint32_t);
+  auto kfn = block_refine_direct_kernel<D, HB>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kfn, dim3(a.B * a.tiles_per_seq), dim3(NW * 64), lds, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_refine(const BlockRefineArgs& a, hipStream_t s) {
-  if (a.q_dtype == DT_BF16 && a.k_dtype == DT_BF16) return launch_br_dh<MmaBf16, DT_BF16>(a, s);
+  if (a.q_dtype == DT_BF16 && a.k_dtype == DT_BF16) {
+    const int HB = (a.H + 31) / 32;
+    const bool pow2 = (a.block_size & (a.block_size - 1)) == 0;
+    if (pow2 && a.D == 128 && HB <= 2) return launch_brd<128, 2>(a, s);
+    if (pow2 && a.D == 64 && HB <= 2) return launch_brd<64, 2>(a, s);
+    return launch_br_dh<MmaBf16, DT_BF16>(a, s);
+  }
   if (a.k_dtype == DT_F32) return launch_br_dh<MmaF32, DT_F32>(a, s);
   if (a.k_dtype == DT_BF16) return launch_br_dh<MmaF32, DT_BF16>(a, s);
   return hipErrorInvalidValue;
