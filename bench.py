@@ -38,13 +38,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def csrc_digest():
-    """sha256 over the kernel sources and build flags (changes whenever a kernel may change)."""
+# source files each profiled kernel is compiled from (its own file and the headers it includes)
+KERNEL_SOURCES = {
+    "score_kernel": ["score.hip", "score_tile.h", "kernels.h"],
+    "decode_scan_kernel": ["decode.hip", "kernels.h"],
+    "block_refine_kernel": ["block_refine.hip", "score_tile.h", "kernels.h"],
+    "block_refine_direct_kernel": ["block_refine.hip", "score_tile.h", "kernels.h"],
+}
+
+
+def csrc_digest(kernel):
+    """sha256 over the sources of `kernel` and the build flags (changes whenever it may change)."""
     import hashlib
     pkg = os.path.join(ROOT, "sparse_attention_indexer_02_amd")
     h = hashlib.sha256()
-    files = sorted(os.path.join(pkg, "csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))
-                   if f.endswith((".hip", ".h")))
+    files = [os.path.join(pkg, "csrc", f) for f in KERNEL_SOURCES[kernel]]
     for f in files + [os.path.join(pkg, "build.py")]:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -59,7 +67,7 @@ def measured_traffic(workload, kernel):
         with open(path) as fh:
             d = json.load(fh)
         e = d["kernels"][f"{kernel}@{workload}"]
-        if e["csrc_sha256"] != csrc_digest():
+        if e["csrc_sha256"] != csrc_digest(kernel):
             return None
         c = d["copy"]
         rf = c["bytes"] / (c["fetch_kib"] * 1024.0)
@@ -67,6 +75,15 @@ def measured_traffic(workload, kernel):
         return e["fetch_kib"] * 1024.0 * rf + e["write_kib"] * 1024.0 * wf
     except (OSError, KeyError, ValueError, ZeroDivisionError):
         return None
+
+
+def block_refine_kernel_name(prob, block_size):
+    """The refine kernel the library dispatches: bf16 queries and keys with a power-of-two block
+    size, D of 64 or 128 and at most 64 heads stream the kept blocks straight into LDS."""
+    import workloads as W
+    direct = (prob.q_dtype == W.BF16 and prob.k_dtype == W.BF16 and block_size & (block_size - 1) == 0
+              and prob.D in (64, 128) and prob.H <= 64)
+    return "block_refine_direct_kernel" if direct else "block_refine_kernel"
 
 
 def copy_probe(nbytes):
@@ -298,9 +315,10 @@ def main():
         ms, n = kernels["block_refine"]
         flops = 2.0 * prob.H * prob.D * rp
         achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "block_refine_kernel", "achieved": achieved,
+        kname = block_refine_kernel_name(prob, spec["block_size"])
+        roof = {"bound": "mfma", "kernel": kname, "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(args.workload, "block_refine_kernel"),
+                "traffic": measured_traffic(args.workload, kname),
                 "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
         cfg.update(block_size=spec["block_size"], n_blocks_keep=spec["n_blocks_keep"],
                    algorithmic_pairs_per_step=cp + rp)
