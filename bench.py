@@ -40,10 +40,10 @@ def log(*a):
 
 # source files each profiled kernel is compiled from (its own file and the headers it includes)
 KERNEL_SOURCES = {
-    "score_kernel": ["score.hip", "score_tile.h", "kernels.h"],
-    "decode_scan_kernel": ["decode.hip", "kernels.h"],
-    "block_refine_kernel": ["block_refine.hip", "score_tile.h", "kernels.h"],
-    "block_refine_direct_kernel": ["block_refine.hip", "score_tile.h", "kernels.h"],
+    "score_kernel": ["score.hip", "score_tile.h", "common.h", "kernels.h"],
+    "decode_scan_kernel": ["decode.hip", "common.h", "kernels.h"],
+    "block_refine_kernel": ["block_refine.hip", "score_tile.h", "common.h", "kernels.h"],
+    "block_refine_direct_kernel": ["block_refine.hip", "score_tile.h", "common.h", "kernels.h"],
 }
 
 

@@ -161,39 +161,44 @@ __device__ __forceinline__ uint32_t wave_bcast(uint32_t x, int lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
 }
 
-// Wave-level search over a histogram of nbins (multiple of 64) bins, highest bin first: the bin
-// holding the need-th largest element (need >= 1) and the count in higher bins. count(b) reads
-// bin b. Returns the total count; *bin_out = -1 when need exceeds it.
+// Wave-level search over a histogram of nbins bins (a power of two, at least 64), highest bin
+// first: the bin holding the need-th largest element (need >= 1) and the count in higher bins.
+// count(b) reads bin b. Returns the total count; *bin_out = -1 when need exceeds it.
+// Lane l sums the contiguous range of nbins/64 bins below nbins - l*nbins/64; the lanes walk
+// their ranges from different offsets, so that one read instruction of the wave touches
+// consecutive bins (distinct LDS banks) instead of 64 bins a bank-count multiple apart. The
+// range that holds the bin is then searched by the whole wave, 64 bins per prefix scan.
 template <class CountFn>
 __device__ __forceinline__ uint32_t wave_hist_find(int nbins, uint32_t need, CountFn count,
                                                    int* bin_out, uint32_t* above_out) {
   const int lane = lane_id();
-  const int per = nbins / 64;
+  const int per = nbins >> 6;
   const int hi = nbins - 1 - lane * per;
   uint32_t sum = 0;
-  for (int i = 0; i < per; ++i) sum += count(hi - i);
+#pragma unroll 8
+  for (int i = 0; i < per; ++i) sum += count(hi - ((i + lane) & (per - 1)));
   const uint32_t inc = wave_scan_dpp(sum);
   const uint32_t tot = wave_bcast(inc, 63);
-  int bin = -1;
-  uint32_t run = inc - sum;
-  if (need > 0 && run < need && need <= inc) {
-    for (int i = 0; i < per; ++i) {
-      const uint32_t h = count(hi - i);
-      if (run + h >= need) {
-        bin = hi - i;
-        break;
-      }
-      run += h;
-    }
-  }
-  const uint64_t m = __ballot(bin >= 0);
+  const uint64_t m = __ballot(need > 0 && inc - sum < need && need <= inc);
+  *bin_out = -1;
+  *above_out = 0;
   if (m) {
     const int src = __builtin_ctzll(m);
-    *bin_out = (int)wave_bcast((uint32_t)bin, src);
-    *above_out = wave_bcast(run, src);
-  } else {
-    *bin_out = -1;
-    *above_out = 0;
+    const int shi = nbins - 1 - src * per;
+    uint32_t base = wave_bcast(inc - sum, src);
+    for (int c = 0; c < per; c += 64) {
+      const int j = c + lane;
+      const uint32_t h = j < per ? count(shi - j) : 0u;
+      const uint32_t s = wave_scan_dpp(h);
+      const uint64_t hit = __ballot(base + s >= need);
+      if (hit) {
+        const int f = __builtin_ctzll(hit);
+        *bin_out = shi - c - f;
+        *above_out = base + wave_bcast(s - h, f);
+        break;
+      }
+      base += wave_bcast(s, 63);
+    }
   }
   return tot;
 }

@@ -40,7 +40,8 @@ score_kernel(ScoreArgs a) {
   int32_t* skey = reinterpret_cast<int32_t*>(smem + 2 * G::TILE_BYTES);   // [2][KT]
   float* sscale = reinterpret_cast<float*>(skey + 2 * KT);                 // [2][KT]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level values stay scalar
   // per-wave histogram of the first radix digit of the row's order-preserving score keys, from
   // which the wave writes its row's selection summary (the selector's first radix pass)
   uint32_t* whist = reinterpret_cast<uint32_t*>(sscale + 2 * KT) + wave * 2048;
@@ -75,8 +76,10 @@ score_kernel(ScoreArgs a) {
   int my_count, key_end;
   if constexpr (!LISTM) {
     my_count = active ? count_of(my_pos) : 0;
-    key_end = 0;
-    for (int u = tb; u < te; ++u) key_end = max(key_end, count_of(a.q_pos[(int64_t)b * a.T + u]));
+    // the tile's key range: the longest prefix of its (at most 64) queries, one load per lane
+    key_end = lane < te - tb ? count_of(a.q_pos[(int64_t)b * a.T + tb + lane]) : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) key_end = max(key_end, __shfl_xor(key_end, o, 64));
   } else {
     key_end = a.list_len[lrow];
     my_count = key_end;
@@ -89,7 +92,7 @@ score_kernel(ScoreArgs a) {
   if (kb0 >= kb1) return;                           // uniform over the work-group
   const int lim = min(my_count, kb1);               // this wave's last slot (exclusive)
   if (fuse)
-    for (int i = lane; i < 2048; i += 64) whist[i] = 0u;
+    for (int i = lane; i < 512; i += 64) reinterpret_cast<u32x4_t*>(whist)[i] = u32x4_t{0u, 0u, 0u, 0u};
 
   // query fragments and head weights of this wave's query
   typename Mma::frag_t qf[HB][G::NKK];
@@ -132,17 +135,24 @@ score_kernel(ScoreArgs a) {
 
   const int ntile = (kb1 - kb0 + KT - 1) / KT;
   Loader ld;
-  // direct path: key indices of the rows this thread's DMA chunks fill, one tile ahead
-  int kidx[DIRECT ? DLoader::ITERS : 1];
+  // direct path, key list: key indices of the rows this thread's DMA chunks fill, read one tile
+  // ahead (a key range computes them when it issues the chunks)
+  int kidx[DIRECT && LISTM ? DLoader::ITERS : 1];
   auto fetch_idx = [&](int base) {
-    if constexpr (DIRECT) {
+    if constexpr (DIRECT && LISTM) {
 #pragma unroll
       for (int i = 0; i < DLoader::ITERS; ++i) kidx[i] = key_at(base, DLoader::row_of(i, wave, lane));
     }
   };
+  auto chunk_key = [&](int base, int i) -> int {
+    if constexpr (LISTM) return kidx[i];
+    else return key_at(base, DLoader::row_of(i, wave, lane));
+  };
   auto issue_tile = [&](int buf, int base) {        // start filling LDS buffer `buf`
     if constexpr (DIRECT) {
-      DLoader::load_idx(kseq, tiles + buf * G::TILE_BYTES, wave, lane, kidx);
+#pragma unroll
+      for (int i = 0; i < DLoader::ITERS; ++i)
+        DLoader::load_chunk(i, kseq, tiles + buf * G::TILE_BYTES, wave, lane, chunk_key(base, i));
       if constexpr (LISTM) {
 #pragma unroll
         for (int i = 0; i < DLoader::ITERS; ++i)
@@ -175,7 +185,12 @@ score_kernel(ScoreArgs a) {
     const int cur = it & 1;
     const int base = kb0 + it * KT;
     const bool more = it + 1 < ntile;
-    if (more) {
+    // bf16 full tiles issue the next tile's loads spread over their MFMA steps (8 waves issuing
+    // all their loads at once queue behind each other and start the tile apart); other tiles
+    // issue them all here
+    const bool full = active && base + KT <= lim;
+    const bool spread = DIRECT && full;
+    if (more && !spread) {
       issue_tile(cur ^ 1, base + KT);
       if constexpr (DIRECT) {
         if (it + 2 < ntile) fetch_idx(base + 2 * KT);
@@ -188,7 +203,7 @@ score_kernel(ScoreArgs a) {
     float ov[NSUB / 2];
 #pragma unroll
     for (int p = 0; p < NSUB / 2; ++p) ov[p] = 0.f;
-    if (active && base + KT <= lim) {
+    if (full) {
       // full tile: the epilogue of each 32-key step overlaps the MFMAs of the next one, and
       // the next step's key fragments are read from LDS while this step's MFMAs run
       f32x16_t A[HB], Bq[HB];
@@ -200,8 +215,20 @@ score_kernel(ScoreArgs a) {
           tile_mma<Mma, D, HB, KT>(qf, tile, s * 32, lane, acc);
         }
       };
+      // the next tile's load chunks [lo, hi) go out during step s; on the last tile they refill
+      // the idle buffer with rows already read (no branch inside the MFMA stream)
+      constexpr int IT = DIRECT ? DLoader::ITERS : 0;
+      auto dma_part = [&](int s) {
+        if constexpr (DIRECT) {
+#pragma unroll
+          for (int i = s * IT / NSUB; i < (s + 1) * IT / NSUB; ++i)
+            DLoader::load_chunk(i, kseq, tiles + (cur ^ 1) * G::TILE_BYTES, wave, lane,
+                                chunk_key(base + KT, i));
+        }
+      };
       if constexpr (DIRECT) load_bfrag<D, KT>(tile, 0, lane, bfr);
       mma_step(0, A);
+      dma_part(0);
 #pragma unroll
       for (int s = 1; s < NSUB; ++s) {
         float tcur;
@@ -213,13 +240,16 @@ score_kernel(ScoreArgs a) {
           mma_step(s, A);
           tcur = tile_epilogue<HB>(Bq, wv);
         }
+        dma_part(s);
         if constexpr (DIRECT) {
           // per key-fragment step: HB MFMAs, one LDS read of the next step, then a slice of
-          // the previous step's epilogue
+          // the previous step's epilogue; this step's load chunks go out after the first MFMAs
+          constexpr int NL = IT / NSUB > 0 ? IT / NSUB : 1;
 #pragma unroll
           for (int kk = 0; kk < G::NKK; ++kk) {
             __builtin_amdgcn_sched_group_barrier(0x008, HB, 0);
             if (s + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (kk == 1) __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, (16 * HB * 2 + 8) / G::NKK + 1, 0);
           }
         }
@@ -228,6 +258,17 @@ score_kernel(ScoreArgs a) {
       }
       const float tl = tile_epilogue<HB>(Bq, wv);
       ov[NSUB / 2 - 1] = lane < 32 ? t_prev : tl;
+      if constexpr (DIRECT) {
+        if (more) {
+          if constexpr (LISTM) {
+#pragma unroll
+            for (int i = 0; i < DLoader::ITERS; ++i)
+              if (DLoader::first_chunk(i, wave, lane))
+                skey[(cur ^ 1) * KT + DLoader::row_of(i, wave, lane)] = kidx[i];
+          }
+          if (it + 2 < ntile) fetch_idx(base + 2 * KT);
+        }
+      }
     } else if (active && base < lim) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
@@ -238,27 +279,34 @@ score_kernel(ScoreArgs a) {
         if ((s & 1) == (lane >> 5)) ov[s / 2] = tot;
       }
     }
-    if (more) {
-      if constexpr (DIRECT) wait_vmem();
-      else ld.store(tiles + (cur ^ 1) * G::TILE_BYTES, tid);
+    if constexpr (DIRECT) {
+      if (more || spread) wait_vmem();
+    } else {
+      if (more) ld.store(tiles + (cur ^ 1) * G::TILE_BYTES, tid);
     }
     if (active) {
+      // every LDS access (scale, key list, histogram) before the score stores: the compiler waits
+      // for all outstanding vector memory operations before an LDS access that follows the LDS
+      // loads of the key tiles, and a store issued earlier would be part of that wait
+      float v[NSUB / 2];
 #pragma unroll
       for (int p = 0; p < NSUB / 2; ++p) {
         const int n = p * 64 + lane;
+        v[p] = ov[p];
         if (base + n < lim) {
-          float v = ov[p];
-          if constexpr (KST == DT_FP8) v *= sscale[cur * KT + n];
+          if constexpr (KST == DT_FP8) v[p] *= sscale[cur * KT + n];
           if constexpr (LISTM) {
-            if (skey[cur * KT + n] > my_pos) v = -INFINITY;
+            if (skey[cur * KT + n] > my_pos) v[p] = -INFINITY;
           }
-          srow[base + n] = v;
           if (fuse) {
-            const uint32_t key = f2key(v);
+            const uint32_t key = f2key(v[p]);
             if (key > KEY_NEG_INF) hist1_add(whist, key, a.digit_bits);
           }
         }
       }
+#pragma unroll
+      for (int p = 0; p < NSUB / 2; ++p)
+        if (base + p * 64 + lane < lim) srow[base + p * 64 + lane] = v[p];
     }
     lds_barrier();
   }

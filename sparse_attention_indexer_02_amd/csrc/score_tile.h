@@ -127,23 +127,27 @@ struct DirectLoader {
     return phys(i, wave, lane) % G::CPR == 0;
   }
 
-  // kidx[i]: key index (row of the sequence's key array) of row_of(i), or -1 for an unused row
+  // The i-th of this lane's chunks: ki = key index (row of the sequence's key array) of
+  // row_of(i), or -1 for an unused row (then row 0 is read and never used).
+  __device__ __forceinline__ static void load_chunk(int i, const uint8_t* kseq, uint8_t* tile,
+                                                    int wave, int lane, int ki) {
+    static_assert(NCH % NTHR == 0, "tile chunks must divide over the work-group");
+    const int blk = i * NWAVE + wave;                // 1 KB LDS block written by this instr
+    const int p = blk * 64 + lane;
+    const int n = p / G::CPR, cp = p % G::CPR;
+    const int c = cp ^ (n & G::SWZ);                 // logical chunk stored at p
+    const uint8_t* src = kseq + (int64_t)(ki >= 0 ? ki : 0) * G::ROW_BYTES + c * 16;
+    __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                              reinterpret_cast<uintptr_t>(tile + blk * 1024)),
+                                     16, 0, 0);
+  }
+
   template <int N>
   __device__ __forceinline__ static void load_idx(const uint8_t* kseq, uint8_t* tile, int wave,
                                                   int lane, const int (&kidx)[N]) {
-    static_assert(NCH % NTHR == 0 && N == ITERS, "tile chunks must divide over the work-group");
+    static_assert(N == ITERS, "one key index per chunk");
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int blk = i * NWAVE + wave;              // 1 KB LDS block written by this instr
-      const int p = blk * 64 + lane;
-      const int n = p / G::CPR, cp = p % G::CPR;
-      const int c = cp ^ (n & G::SWZ);               // logical chunk stored at p
-      const int ki = kidx[i];
-      const uint8_t* src = kseq + (int64_t)(ki >= 0 ? ki : 0) * G::ROW_BYTES + c * 16;
-      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                                reinterpret_cast<uintptr_t>(tile + blk * 1024)),
-                                       16, 0, 0);
-    }
+    for (int i = 0; i < ITERS; ++i) load_chunk(i, kseq, tile, wave, lane, kidx[i]);
   }
 };
 
