@@ -210,16 +210,25 @@ __device__ __forceinline__ uint32_t wave_hist_find(const uint32_t* hist, int nbi
 
 // First radix digit of a selection: the top `bits` (11 or 12) bits of the order-preserving key.
 // With 12 bits the 4096 counters are 16-bit halves of 2048 words (valid for rows of fewer than
-// 65536 slots, so that no half can carry into its neighbour).
+// 65536 slots, so that no half can carry into its neighbour); bins b and b + 2048 (keys of
+// opposite sign) share a word, so that neighbouring bins, which a row's scores crowd into, sit
+// in different words and banks and atomic adds to them do not serialise.
 __device__ __forceinline__ uint32_t digit1(uint32_t key, int bits) { return key >> (32 - bits); }
 
 __device__ __forceinline__ void hist1_add(uint32_t* words, uint32_t key, int bits) {
-  if (bits == 12) atomicAdd(&words[key >> 21], 1u << (((key >> 20) & 1u) * 16));
+  if (bits == 12) atomicAdd(&words[(key >> 20) & 2047u], 1u << ((key >> 31) * 16));
   else atomicAdd(&words[key >> 21], 1u);
 }
 
+// hist1_add without a branch: adds 0 when `ok` is false.
+__device__ __forceinline__ void hist1_add_if(uint32_t* words, uint32_t key, int bits, bool ok) {
+  const uint32_t w = bits == 12 ? (key >> 20) & 2047u : key >> 21;
+  const uint32_t inc = bits == 12 ? 1u << ((key >> 31) * 16) : 1u;
+  atomicAdd(&words[w], ok ? inc : 0u);
+}
+
 __device__ __forceinline__ uint32_t hist1_count(const uint32_t* words, int bin, int bits) {
-  if (bits == 12) return (words[bin >> 1] >> ((bin & 1) * 16)) & 0xFFFFu;
+  if (bits == 12) return (words[bin & 2047] >> ((bin >> 11) * 16)) & 0xFFFFu;
   return words[bin];
 }
 

@@ -32,6 +32,7 @@ score_kernel(ScoreArgs a) {
   constexpr int KT = TileKeys<Mma, KST>::value;
   constexpr int NSUB = KT / 32;
   constexpr bool META = LISTM || KST == DT_FP8;
+  static_assert(!Direct<Mma, KST>::value || NSUB >= 2, "direct tiles span several 32-key steps");
   typedef Geo<Mma, D, KT> G;
   typedef TileLoader<Mma, D, KST, NTHR, KT> Loader;
   typedef DirectLoader<D, NTHR, KT> DLoader;
@@ -77,9 +78,10 @@ score_kernel(ScoreArgs a) {
   if constexpr (!LISTM) {
     my_count = active ? count_of(my_pos) : 0;
     // the tile's key range: the longest prefix of its (at most 64) queries, one load per lane
-    key_end = lane < te - tb ? count_of(a.q_pos[(int64_t)b * a.T + tb + lane]) : 0;
+    const int c = lane < te - tb ? count_of(a.q_pos[(int64_t)b * a.T + tb + lane]) : 0;
+    key_end = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) key_end = max(key_end, __shfl_xor(key_end, o, 64));
+    for (int u = 0; u < NW; ++u) key_end = max(key_end, __builtin_amdgcn_readlane(c, u));
   } else {
     key_end = a.list_len[lrow];
     my_count = key_end;
@@ -100,21 +102,39 @@ score_kernel(ScoreArgs a) {
   {
     const int hh = lane >> 5, ln = lane & 31;
     const int qeb = dtype_bytes(a.q_dtype);
+    const float* wrow = a.w + ((int64_t)b * a.T + (active ? t : 0)) * a.H;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const int head = 32 * hb + ln;
       const bool ok = active && head < a.H;
       const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
                             (((int64_t)b * a.T + (ok ? t : 0)) * a.H + (ok ? head : 0)) * D * qeb;
+      // a head block the query fills: plain loads (no per-lane branches); the weights of the
+      // 16 heads a lane accumulates are 4 runs of 4 consecutive heads
+      if (active && 32 * hb + 32 <= a.H) {
 #pragma unroll
-      for (int kk = 0; kk < G::NKK; ++kk) {
-        if (ok) qf[hb][kk] = load_frag<Mma>(qrow, a.q_dtype, hh * (D / 2) + kk * Mma::E);
-        else qf[hb][kk] = typename Mma::frag_t{};
+        for (int kk = 0; kk < G::NKK; ++kk)
+          qf[hb][kk] = load_frag<Mma>(qrow, a.q_dtype, hh * (D / 2) + kk * Mma::E);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < G::NKK; ++kk) {
+          if (ok) qf[hb][kk] = load_frag<Mma>(qrow, a.q_dtype, hh * (D / 2) + kk * Mma::E);
+          else qf[hb][kk] = typename Mma::frag_t{};
+        }
       }
+      if (active && 32 * hb + 32 <= a.H && (a.H & 3) == 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int h = acc_head(hb, r, lane);
-        wv[hb][r] = (active && h < a.H) ? a.w[((int64_t)b * a.T + t) * a.H + h] : 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(wrow + 32 * hb + 8 * j + 4 * hh);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wv[hb][4 * j + i] = v[i];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int h = acc_head(hb, r, lane);
+          wv[hb][r] = (active && h < a.H) ? wrow[h] : 0.f;
+        }
       }
     }
   }
@@ -181,10 +201,34 @@ score_kernel(ScoreArgs a) {
   float* srow = a.scores + ((int64_t)b * a.rows_per_seq + (active ? t - row0 : 0)) * a.score_stride;
   bf16x8_t bfr[DIRECT ? G::NKK : 1];                 // rotating key fragments (bf16 path)
 
+  // Scores of a full tile are counted and stored at the start of the next tile, before its
+  // first load: the compiler waits for every outstanding vector memory operation before an LDS
+  // access that follows the tiles' LDS loads, so the histogram adds must not come after a
+  // load; and at the end of the tile they would hold every wave up at the tile barrier.
+  float pv[NSUB / 2];
+  int pbase = -1;                                     // first slot of the pending scores, or -1
+#pragma unroll
+  for (int p = 0; p < NSUB / 2; ++p) pv[p] = 0.f;
+  auto flush = [&]() {
+    if (pbase >= 0) {
+      if (fuse) {
+#pragma unroll
+        for (int p = 0; p < NSUB / 2; ++p) {
+          const uint32_t key = f2key(pv[p]);
+          hist1_add_if(whist, key, a.digit_bits, key > KEY_NEG_INF);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < NSUB / 2; ++p) srow[pbase + p * 64 + lane] = pv[p];
+      pbase = -1;
+    }
+  };
+
   for (int it = 0; it < ntile; ++it) {
     const int cur = it & 1;
     const int base = kb0 + it * KT;
     const bool more = it + 1 < ntile;
+    flush();
     // bf16 full tiles issue the next tile's loads spread over their MFMA steps (8 waves issuing
     // all their loads at once queue behind each other and start the tile apart); other tiles
     // issue them all here
@@ -197,9 +241,7 @@ score_kernel(ScoreArgs a) {
       }
     }
     const uint8_t* tile = tiles + cur * G::TILE_BYTES;
-    // scores of this tile, two 32-key steps per value (lanes 0-31: even step, 32-63: odd step),
-    // kept in registers and stored after the wait for the next tile's loads, so that the wait
-    // never waits on this tile's stores
+    // scores of this tile, two 32-key steps per value (lanes 0-31: even step, 32-63: odd step)
     float ov[NSUB / 2];
 #pragma unroll
     for (int p = 0; p < NSUB / 2; ++p) ov[p] = 0.f;
@@ -215,13 +257,14 @@ score_kernel(ScoreArgs a) {
           tile_mma<Mma, D, HB, KT>(qf, tile, s * 32, lane, acc);
         }
       };
-      // the next tile's load chunks [lo, hi) go out during step s; on the last tile they refill
-      // the idle buffer with rows already read (no branch inside the MFMA stream)
+      // the next tile's load chunks go out during the first NSUB - 1 steps (chunk i in step
+      // i (NSUB - 1) / IT), so that the last has a whole step to land; on the last tile they
+      // refill the idle buffer with rows already read (no branch inside the MFMA stream)
       constexpr int IT = DIRECT ? DLoader::ITERS : 0;
       auto dma_part = [&](int s) {
         if constexpr (DIRECT) {
 #pragma unroll
-          for (int i = s * IT / NSUB; i < (s + 1) * IT / NSUB; ++i)
+          for (int i = (s * IT + NSUB - 2) / (NSUB - 1); i < ((s + 1) * IT + NSUB - 2) / (NSUB - 1) && i < IT; ++i)
             DLoader::load_chunk(i, kseq, tiles + (cur ^ 1) * G::TILE_BYTES, wave, lane,
                                 chunk_key(base + KT, i));
         }
@@ -284,10 +327,19 @@ score_kernel(ScoreArgs a) {
     } else {
       if (more) ld.store(tiles + (cur ^ 1) * G::TILE_BYTES, tid);
     }
-    if (active) {
-      // every LDS access (scale, key list, histogram) before the score stores: the compiler waits
-      // for all outstanding vector memory operations before an LDS access that follows the LDS
-      // loads of the key tiles, and a store issued earlier would be part of that wait
+    if (full && !LISTM) {
+#pragma unroll
+      for (int p = 0; p < NSUB / 2; ++p) {
+        const int n = p * 64 + lane;
+        pv[p] = ov[p];
+        if constexpr (KST == DT_FP8) pv[p] *= sscale[cur * KT + n];
+        if constexpr (LISTM) {
+          if (skey[cur * KT + n] > my_pos) pv[p] = -INFINITY;
+        }
+      }
+      pbase = base;
+    } else if (active) {
+      // partial tile: every LDS access (scale, key list, histogram) before the score stores
       float v[NSUB / 2];
 #pragma unroll
       for (int p = 0; p < NSUB / 2; ++p) {
@@ -310,12 +362,18 @@ score_kernel(ScoreArgs a) {
     }
     lds_barrier();
   }
+  flush();
   if (fuse && active) {
     int bin;
     uint32_t above;
     const int bits = a.digit_bits;
+    // bin q's count without a branch on the digit width (12 bits: bins q and q + 2048 are the
+    // 16-bit halves of word q mod 2048)
+    const uint32_t hm = bits == 12 ? 0xFFFFu : 0xFFFFFFFFu;
+    const int hsh = bits == 12 ? 11 : 31;
     const uint32_t tot = wave_hist_find(1 << bits, (uint32_t)a.topk_k,
-                                        [&](int q) { return hist1_count(whist, q, bits); }, &bin, &above);
+                                        [&](int q) { return (whist[q & 2047] >> ((q >> hsh) << 4)) & hm; },
+                                        &bin, &above);
     if (lane == 0) {
       int32_t* m = a.row_meta + ((int64_t)b * a.rows_per_seq + (t - row0)) * 4;
       m[META_NVALID] = (int32_t)tot;
