@@ -217,6 +217,7 @@ int cu_count() {
 struct DecodePlan {
   int nchunk, chunk, sub, nsegs, cand_cap;
   uint32_t* ccount;
+  uint32_t* shist;
   uint32_t* cand_key;
   uint32_t* cand_idx;
   uint32_t* cand2_key;
@@ -241,6 +242,7 @@ DecodePlan plan_decode(const idx_problem* p, void* ws) {
   d.nsegs = (p->N + d.sub - 1) / d.sub;
   d.cand_cap = (int)rstride(p->N);
   d.ccount = c.take<uint32_t>((size_t)rows * d.nsegs);
+  d.shist = c.take<uint32_t>((size_t)rows * d.nsegs * (DECODE_BINS / 2));
   d.cand_key = c.take<uint32_t>((size_t)rows * d.cand_cap);
   d.cand_idx = c.take<uint32_t>((size_t)rows * d.cand_cap);
   d.cand2_key = c.take<uint32_t>((size_t)rows * d.cand_cap);
@@ -316,7 +318,7 @@ int decode_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_sc
   a.keys = p->k; a.k_dtype = p->k_dtype; a.k_scale = p->k_scale; a.k_len = p->k_len;
   a.B = p->B; a.T = p->T; a.H = p->H; a.D = p->D; a.N = p->N;
   a.nchunk = pl.nchunk; a.chunk = pl.chunk; a.sub = pl.sub;
-  a.ccount = pl.ccount; a.nsegs = pl.nsegs;
+  a.ccount = pl.ccount; a.nsegs = pl.nsegs; a.shist = pl.shist;
   a.cand_key = pl.cand_key; a.cand_idx = pl.cand_idx;
   a.cand2_key = pl.cand2_key; a.cand2_idx = pl.cand2_idx; a.cand_cap = pl.cand_cap;
   a.k = k;

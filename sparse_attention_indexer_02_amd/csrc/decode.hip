@@ -25,6 +25,7 @@
 // decode_select_kernel: work-group = row. The top-k of the row's candidates (radix select over
 //   the order-preserving keys, ties to the lowest slots) and the padding.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -293,12 +294,17 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     static_assert(BPT % 8 == 0, "whole 16-byte reads of packed bins");
     uint32_t bins[2][BPT];
     uint32_t part = 0;
+    const int seg = sub0 / a.sub;
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       uint32_t sum = 0;
+      // the selector sums the sub-chunks' histograms (every key in a bin at or above a
+      // sub-chunk's bound is one of its candidates)
+      uint32_t* hout = a.shist + ((qq ? r1 : r0) * a.nsegs + seg) * (DC_BINS / 2) + 2048 - (BPT / 2) * (tid + 1);
 #pragma unroll
       for (int c = 0; c < BPT / 8; ++c) {
         const u32x4_t w = *reinterpret_cast<const u32x4_t*>(hist + qq * 2048 + 2048 - (BPT / 2) * (tid + 1) + 4 * c);
+        if (qq < nrows) reinterpret_cast<u32x4_t*>(hout)[c] = w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           bins[qq][8 * c + 2 * e] = w[e] & 0xFFFFu;
@@ -419,6 +425,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
 constexpr int RS_THREADS = 512;
 constexpr int RS_WAVES = RS_THREADS / 64;
 constexpr int RS_LDS_CAND = 4096;
+constexpr int RS_R = 64;                                  // candidate chunks held in registers
 
 __device__ __forceinline__ void block_find_desc(const uint32_t* h, uint32_t need, uint32_t* sh, uint32_t* out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -467,6 +474,9 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
   __shared__ uint32_t ckey[RS_LDS_CAND];
   __shared__ uint32_t cpos[RS_LDS_CAND];
   __shared__ uint32_t sh[RS_WAVES];
+  __shared__ uint32_t wsum[2 * RS_WAVES];
+  __shared__ __align__(16) uint32_t cbase[RS_R];
+  __shared__ __align__(16) int clim[RS_R];
   __shared__ uint32_t bc[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t r = blockIdx.x;
@@ -500,26 +510,70 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  // visits every candidate (key, position in the list), 4 loads per thread in flight
-  auto for_each = [&](auto f) {
-    for (int sg = 0; sg < a.nsegs; ++sg) {
+  // Visits the candidates in batches of RS_U * RS_THREADS of one segment (key, and slot when
+  // IDX), the next batch's loads in flight while f runs on the current one: f(ok[], x[], i[]).
+  constexpr int RS_U = 4;
+  struct Batch {
+    uint32_t x[RS_U], i[RS_U];
+    bool ok[RS_U];
+  };
+  auto advance = [&](int& sg, int& j0) {                  // next batch (uniform)
+    j0 += RS_U * RS_THREADS;
+    while (sg < a.nsegs && j0 >= (int)counts[sg]) {
+      ++sg;
+      j0 = 0;
+    }
+  };
+  auto for_batches = [&](auto f, auto idx_tag) {
+    constexpr bool IDX = decltype(idx_tag)::value;
+    auto load = [&](int sg, int j0, Batch& bt) {
       const int c = (int)counts[sg];
       const uint32_t base = (uint32_t)sg * (uint32_t)a.sub;
-      for (int j0 = 0; j0 < c; j0 += 4 * RS_THREADS) {
-        uint32_t x[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = gk[base + min(j0 + u * RS_THREADS + tid, c - 1)];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) f(j0 + u * RS_THREADS + tid < c, x[u], base + j0 + u * RS_THREADS + tid);
+      for (int u = 0; u < RS_U; ++u) {
+        const int j = j0 + u * RS_THREADS + tid;
+        const uint32_t p = base + (uint32_t)min(j, c - 1);
+        bt.ok[u] = j < c;
+        bt.x[u] = gk[p];
+        if constexpr (IDX) bt.i[u] = gi[p];
+        else bt.i[u] = 0u;
       }
+    };
+    int sg = 0, j0 = -RS_U * RS_THREADS;
+    advance(sg, j0);
+    Batch A, B;
+    if (sg < a.nsegs) load(sg, j0, A);
+    while (sg < a.nsegs) {
+      advance(sg, j0);
+      if (sg < a.nsegs) load(sg, j0, B);
+      f(A);
+      if (sg >= a.nsegs) break;
+      advance(sg, j0);
+      if (sg < a.nsegs) load(sg, j0, A);
+      f(B);
     }
   };
 
-  // ---- pass 1: first-digit histogram, bin b1 of the kk-th largest
+  // ---- first-digit histogram and bin b1 of the kk-th largest: the sum of the sub-chunks'
+  // histograms, exact in every bin at or above the highest sub-chunk bound. Some sub-chunk
+  // holds k keys at or above its own bound when M > kk, so b1 is at or above every bound.
   if (!all) {
-    for_each([&](bool ok, uint32_t x, uint32_t) {
-      if (ok) atomicAdd(&hist[x >> 20], 1u);
-    });
+    const int lo = DC_BINS - 8 * (tid + 1);               // this thread's bins [lo, lo + 8)
+    uint32_t hs[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    const uint32_t* src = a.shist + r * a.nsegs * (DC_BINS / 2) + lo / 2;
+#pragma unroll 4
+    for (int sg = 0; sg < a.nsegs; ++sg) {
+      // a sub-chunk without candidates has no keys (and a histogram that was never written)
+      const uint32_t keep = counts[sg] ? ~0u : 0u;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + (size_t)sg * (DC_BINS / 2));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hs[2 * e] += v[e] & 0xFFFFu & keep;
+        hs[2 * e + 1] += (v[e] >> 16) & keep;
+      }
+    }
+    *reinterpret_cast<u32x4_t*>(hist + lo) = u32x4_t{hs[0], hs[1], hs[2], hs[3]};
+    *reinterpret_cast<u32x4_t*>(hist + lo + 4) = u32x4_t{hs[4], hs[5], hs[6], hs[7]};
   }
   __syncthreads();
   uint32_t b1 = 0, above = 0;
@@ -530,46 +584,157 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
   }
 
   // ---- pass 2: candidates above b1 out (all when every candidate is selected), bin b1 kept
-  // as (key, position in the list)
-  if (kk > 0) {
-    for_each([&](bool ok, uint32_t x, uint32_t p) {
-      const bool sel = ok && (all || (x >> 20) > b1);
-      const bool cand = ok && !all && (x >> 20) == b1;
-      const uint64_t ms = __ballot(sel), mc = __ballot(cand);
-      uint32_t ps = 0, pc = 0;
-      if (lane == 0) {
-        if (ms) ps = atomicAdd(&bc[4], (uint32_t)__popcll(ms));
-        if (mc) pc = atomicAdd(&bc[5], (uint32_t)__popcll(mc));
+  // as (key, slot). Up to RS_R chunks of RS_THREADS candidates (one segment each) are loaded
+  // at once and held in registers; a row with more streams them in batches instead.
+  // chunk table: chunk u = candidates [cbase[u], cbase[u] + clim[u]) of one segment, at most
+  // RS_THREADS; held when every candidate is in the first RS_R chunks (and there are at most
+  // 64 segments: lane g of wave 0 lays out segment g's chunks)
+  if (wave == 0) {
+    const int c = lane < a.nsegs ? (int)counts[lane] : 0;
+    const uint32_t nch = (uint32_t)(c + RS_THREADS - 1) / RS_THREADS;
+    const uint32_t inc = wave_scan_dpp(nch);
+    const uint32_t tot = wave_bcast(inc, 63);
+    const bool fits = a.nsegs <= 64 && tot <= (uint32_t)RS_R;
+    if (fits) {
+      for (uint32_t q = 0; q < nch; ++q) {
+        const uint32_t u = inc - nch + q;
+        cbase[u] = (uint32_t)lane * (uint32_t)a.sub + q * RS_THREADS;
+        clim[u] = min(c - (int)(q * RS_THREADS), RS_THREADS);
       }
-      const uint32_t bs = __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
-      const uint32_t bcn = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
-      if (sel) {
-        const uint32_t pos = wave_bcast(ps, 0) + bs;
-        oidx[pos] = (int32_t)gi[p];
-        if (osc) osc[pos] = key2f(x);
+      for (uint32_t u = tot + lane; u < (uint32_t)RS_R; u += 64) {
+        cbase[u] = 0u;
+        clim[u] = 0;
       }
-      if (cand) {
-        const uint32_t cp = wave_bcast(pc, 0) + bcn;
-        if (cp < (uint32_t)RS_LDS_CAND) {
-          ckey[cp] = x;
-          cpos[cp] = p;
-        } else {
-          g2k[cp] = x;
-          g2p[cp] = p;
+    }
+    if (lane == 0) bc[6] = fits ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool held = kk > 0 && bc[6] != 0u;
+  if (held) {
+    // keys; 0 (below every finite score's key) where a chunk has no candidate
+    uint32_t xr[RS_R], ir[RS_R];                           // key and slot
+#pragma unroll
+    for (int u = 0; u < RS_R; u += 4) {
+      const u32x4_t cb = *reinterpret_cast<const u32x4_t*>(cbase + u);
+      const int4 cl = *reinterpret_cast<const int4*>(clim + u);
+      const int lim[4] = {cl.x, cl.y, cl.z, cl.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xr[u + e] = 0u;
+        ir[u + e] = 0u;
+        if (tid < lim[e]) {
+          xr[u + e] = gk[cb[e] + (uint32_t)tid];
+          ir[u + e] = gi[cb[e] + (uint32_t)tid];
         }
       }
-    });
+    }
+    // selected: above b1 (every candidate when all are taken); bin-b1 candidates: in b1
+    auto is_sel = [&](uint32_t x, uint32_t bb) { return (x > KEY_NEG_INF) & (all | ((x >> 20) > bb)); };
+    auto is_cand = [&](uint32_t x, uint32_t bb) { return (x > KEY_NEG_INF) & !all & ((x >> 20) == bb); };
+    // per-wave counts, then each wave writes its candidates from its own offsets
+    uint32_t cs = 0, cq = 0;                               // this lane's counts
+#pragma unroll
+    for (int u = 0; u < RS_R; ++u) {
+      cs += is_sel(xr[u], b1) ? 1u : 0u;
+      cq += is_cand(xr[u], b1) ? 1u : 0u;
+    }
+    cs = wave_scan_dpp(cs);
+    cq = wave_scan_dpp(cq);
+    if (lane == 63) {
+      wsum[wave] = cs;
+      wsum[RS_WAVES + wave] = cq;
+    }
+    __syncthreads();
+    uint32_t ps = 0, pc = 0;
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) {
+      ps += w < wave ? wsum[w] : 0u;
+      pc += w < wave ? wsum[RS_WAVES + w] : 0u;
+    }
+    if (tid == 0) {
+      uint32_t ts = 0, tq = 0;
+#pragma unroll
+      for (int w = 0; w < RS_WAVES; ++w) {
+        ts += wsum[w];
+        tq += wsum[RS_WAVES + w];
+      }
+      bc[4] = ts;
+      bc[5] = tq;
+    }
+    // the masks are recomputed below rather than kept from the count loop (RS_R x 2 masks)
+    uint32_t b1x = b1;
+    asm volatile("" : "+v"(b1x));
+#pragma unroll
+    for (int u = 0; u < RS_R; ++u) asm volatile("" : "+v"(xr[u]));
+#pragma unroll
+    for (int u = 0; u < RS_R; ++u) {
+      const bool sel = is_sel(xr[u], b1x), cand = is_cand(xr[u], b1x);
+      const uint64_t ms = __ballot(sel), mc = __ballot(cand);
+      const uint32_t sl = ir[u];
+      if (sel) {
+        const uint32_t pos = ps + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
+        oidx[pos] = (int32_t)sl;
+        if (osc) osc[pos] = key2f(xr[u]);
+      }
+      if (cand) {
+        const uint32_t cp = pc + __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
+        if (cp < (uint32_t)RS_LDS_CAND) {
+          ckey[cp] = xr[u];
+          cpos[cp] = sl;
+        } else {
+          g2k[cp] = xr[u];
+          g2p[cp] = sl;
+        }
+      }
+      ps += (uint32_t)__popcll(ms);
+      pc += (uint32_t)__popcll(mc);
+    }
+  }
+  if (kk > 0 && !held) {
+    for_batches([&](const Batch& bt) {
+      uint64_t ms[RS_U], mc[RS_U];
+      uint32_t ns = 0, nq = 0;
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) {
+        ms[u] = __ballot(bt.ok[u] && (all || (bt.x[u] >> 20) > b1));
+        mc[u] = __ballot(bt.ok[u] && !all && (bt.x[u] >> 20) == b1);
+        ns += (uint32_t)__popcll(ms[u]);
+        nq += (uint32_t)__popcll(mc[u]);
+      }
+      uint32_t ps = 0, pc = 0;
+      if (lane == 0) {
+        if (ns) ps = atomicAdd(&bc[4], ns);
+        if (nq) pc = atomicAdd(&bc[5], nq);
+      }
+      ps = wave_bcast(ps, 0);
+      pc = wave_bcast(pc, 0);
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) {
+        const uint32_t bs = __builtin_amdgcn_mbcnt_hi((uint32_t)(ms[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms[u], 0u));
+        const uint32_t bq = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mc[u], 0u));
+        if ((ms[u] >> lane) & 1u) {
+          oidx[ps + bs] = (int32_t)bt.i[u];
+          if (osc) osc[ps + bs] = key2f(bt.x[u]);
+        }
+        if ((mc[u] >> lane) & 1u) {
+          const uint32_t cp = pc + bq;
+          if (cp < (uint32_t)RS_LDS_CAND) {
+            ckey[cp] = bt.x[u];
+            cpos[cp] = bt.i[u];
+          } else {
+            g2k[cp] = bt.x[u];
+            g2p[cp] = bt.i[u];
+          }
+        }
+        ps += (uint32_t)__popcll(ms[u]);
+        pc += (uint32_t)__popcll(mc[u]);
+      }
+    }, std::true_type{});
   }
   __syncthreads();
 
   if (kk > 0 && !all) {
     const uint32_t nc = bc[5];
-    // slots of the bin-b1 candidates (their list positions are replaced by the slots)
-    for (uint32_t j = tid; j < nc; j += RS_THREADS) {
-      if (j < (uint32_t)RS_LDS_CAND) cpos[j] = gi[cpos[j]];
-      else g2p[j] = gi[g2p[j]];
-    }
-    __syncthreads();
     auto get = [&](uint32_t j, uint32_t& x, uint32_t& i) {
       if (j < (uint32_t)RS_LDS_CAND) {
         x = ckey[j];
