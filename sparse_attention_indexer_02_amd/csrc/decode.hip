@@ -58,10 +58,6 @@ __device__ __forceinline__ int frag_d0(int s, int g) {
   return KST == DT_FP8 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
 }
 
-// Count of bin bb in a histogram of 4096 bins held as 16-bit halves of 2048 words.
-__device__ __forceinline__ uint32_t h16(const uint32_t* w, int bb) {
-  return (w[bb >> 1] >> ((bb & 1) * 16)) & 0xFFFFu;
-}
 
 template <int D, int HB, int KST, int PF>
 __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a) {
@@ -117,10 +113,15 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + frag_d0<KST>(s, g));
         qf[j][hb][s] = ok ? __builtin_bit_cast(bf16x8_t, v) : bf16x8_t{};
       }
+      const int h0 = 16 * hb + 4 * g;                              // 4 consecutive heads
+      if ((a.H & 3) == 0) {
+        const f32x4_t v = h0 < a.H ? *reinterpret_cast<const f32x4_t*>(a.w + rr * a.H + h0) : f32x4_t{};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 16 * hb + 4 * g + r;
-        wv[j][hb][r] = a.w[rr * a.H + min(h, a.H - 1)] * (h < a.H ? 1.f : 0.f);
+        for (int r = 0; r < 4; ++r) wv[j][hb][r] = v[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          wv[j][hb][r] = a.w[rr * a.H + min(h0 + r, a.H - 1)] * (h0 + r < a.H ? 1.f : 0.f);
       }
     }
   }
@@ -138,11 +139,8 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
   const uint32_t lane_koff = 16u * g;
   const bool owner = g == 0 || (g == 1 && two);                    // lanes that emit a score
   const int oq = (g == 1 && two) ? 1 : 0;                          // and the row they emit for
-  const int oP = oq ? P1 : P0;
   float* my_ssc = ssc + oq * a.sub;
-  uint32_t* my_hist = hist + oq * 2048;
   float* sink_f = reinterpret_cast<float*>(sink) + lane;            // writes of masked lanes
-  uint32_t* sink_h = sink + 64 + lane;
 
   for (int sub0 = c0; sub0 < c1; sub0 += a.sub) {
     const int sub1 = min(sub0 + a.sub, c1);
@@ -231,9 +229,6 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
         const int jl = (i * DC_WAVES + wave) * DC_KB + n;             // offset in the sub-chunk
         const bool valid = owner & ((unsigned)jl < (unsigned)(sub1 - sub0));
         *(valid ? my_ssc + jl : sink_f) = v;
-        const uint32_t key = f2key(v);
-        const bool hv = valid & (sub0 + jl < oP) & (key > KEY_NEG_INF);
-        atomicAdd(hv ? my_hist + (key >> 21) : sink_h, 1u << (((key >> 20) & 1u) * 16));
       }
     };
     auto epilogue = [&](int i, const f32x4v_t (&ac)[2][HB], float sc) {
@@ -286,6 +281,25 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     epilogue(iters - 1, acc[1], scl[PF - 1]);                      // iters is a multiple of even PF
     __syncthreads();
 
+    // ---- first-digit histogram of each row's scores in the sub-chunk (its visible keys), from
+    // LDS after the block loop: kept out of the loop, whose VALU issue is the bottleneck
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      if (qq < nrows) {
+        const int lim = min(sub1, qq ? P1 : P0) - sub0;               // visible slots
+        uint32_t* hq = hist + qq * 2048;
+        for (int j = 4 * tid; j < lim; j += 4 * DC_THREADS) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ssc + qq * a.sub + j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = f2key(v[e]);
+            if ((j + e < lim) & (key > KEY_NEG_INF)) atomicAdd(hq + ((key >> 20) & 2047u), 1u << ((key >> 31) * 16));
+          }
+        }
+      }
+    }
+    __syncthreads();
+
     // ---- end of the sub-chunk. Thread t owns first-digit bins [4096 - BPT (t+1), 4096 - BPT t)
     // of both rows and finds the bin b of each row's k-th largest score in this sub-chunk (both
     // rows' counts packed in one word: each <= DC_SUB).
@@ -295,22 +309,22 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     uint32_t bins[2][BPT];
     uint32_t part = 0;
     const int seg = sub0 / a.sub;
+    const int blo = DC_BINS - BPT * (tid + 1);                     // bins [blo, blo + BPT)
+    const int w0 = blo & 2047, hsh = blo >= 2048 ? 16 : 0;         // their words and half
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       uint32_t sum = 0;
       // the selector sums the sub-chunks' histograms (every key in a bin at or above a
-      // sub-chunk's bound is one of its candidates)
-      uint32_t* hout = a.shist + ((qq ? r1 : r0) * a.nsegs + seg) * (DC_BINS / 2) + 2048 - (BPT / 2) * (tid + 1);
+      // sub-chunk's bound is one of its candidates); threads 0-127 hold every word once
+      uint32_t* hout = a.shist + ((qq ? r1 : r0) * a.nsegs + seg) * (DC_BINS / 2) + w0;
 #pragma unroll
-      for (int c = 0; c < BPT / 8; ++c) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(hist + qq * 2048 + 2048 - (BPT / 2) * (tid + 1) + 4 * c);
-        if (qq < nrows) reinterpret_cast<u32x4_t*>(hout)[c] = w;
+      for (int c = 0; c < BPT / 4; ++c) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(hist + qq * 2048 + w0 + 4 * c);
+        if ((qq < nrows) & (tid < 128)) reinterpret_cast<u32x4_t*>(hout)[c] = w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          bins[qq][8 * c + 2 * e] = w[e] & 0xFFFFu;
-          bins[qq][8 * c + 2 * e + 1] = w[e] >> 16;
-          sum += w[e] & 0xFFFFu;
-          sum += w[e] >> 16;
+          bins[qq][4 * c + e] = (w[e] >> hsh) & 0xFFFFu;
+          sum += bins[qq][4 * c + e];
         }
       }
       part |= sum << (16 * qq);
@@ -355,11 +369,12 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     // candidate of one sub-chunk only), and their count to the sub-chunk's counter
     if (tid < nrows) a.ccount[(tid ? r1 : r0) * a.nsegs + sub0 / a.sub] = misc[4 * tid + 1];
     // ---- candidates (order-preserving key, slot) at or above each row's bound. Wave w takes
-    // the slots j with (j / 256) % DC_WAVES == w, 4 per lane per step: a first pass counts them
-    // (ballots), the waves' counts are prefix-summed, a second pass writes them.
+    // the slots j with (j / 256) % DC_WAVES == w, 4 per lane per step: a first pass counts them,
+    // the waves' counts are prefix-summed, a second pass compacts each step's candidates in the
+    // wave's LDS staging area (the histogram's, free again) and writes them as contiguous runs.
     const int len = sub1 - sub0;
     const int steps = (len + 4 * DC_THREADS - 1) / (4 * DC_THREADS);
-    auto sel_masks = [&](int qq, int st, uint32_t thr, uint32_t (&key)[4], uint64_t (&m)[4]) {
+    auto sel_flags = [&](int qq, int st, uint32_t thr, uint32_t (&key)[4], bool (&f)[4]) {
       const int j0 = st * 4 * DC_THREADS + wave * 256 + 4 * lane;
       const int jr = min(j0, a.sub - 4);
       const int lim = min(len, (qq ? P1 : P0) - sub0);
@@ -367,7 +382,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         key[e] = f2key(v[e]);
-        m[e] = __ballot(j0 + e < lim && key[e] >= thr);
+        f[e] = (j0 + e < lim) & (key[e] >= thr);
       }
     };
     uint32_t wcnt[2] = {0u, 0u};
@@ -375,13 +390,16 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     for (int qq = 0; qq < 2; ++qq) {
       if (qq < nrows) {
         const uint32_t thr = misc[4 * qq];
+        uint32_t c = 0;
+#pragma unroll 4
         for (int st = 0; st < steps; ++st) {
           uint32_t key[4];
-          uint64_t m[4];
-          sel_masks(qq, st, thr, key, m);
+          bool f[4];
+          sel_flags(qq, st, thr, key, f);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wcnt[qq] += (uint32_t)__popcll(m[e]);
+          for (int e = 0; e < 4; ++e) c += f[e] ? 1u : 0u;
         }
+        wcnt[qq] = wave_bcast(wave_scan_dpp(c), 63);
       }
     }
     if (lane == 0) {
@@ -389,6 +407,8 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
       misc[24 + wave] = wcnt[1];
     }
     __syncthreads();
+    uint32_t* stage_k = hist + wave * 512;                        // [256] keys, [256] slots
+    uint32_t* stage_i = stage_k + 256;
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       if (qq < nrows) {
@@ -400,18 +420,26 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
         uint32_t* ci = a.cand_idx + rr * a.cand_cap;
         for (int st = 0; st < steps; ++st) {
           uint32_t key[4];
-          uint64_t m[4];
-          sel_masks(qq, st, thr, key, m);
+          bool f[4];
+          sel_flags(qq, st, thr, key, f);
           const uint32_t jb = (uint32_t)(sub0 + st * 4 * DC_THREADS + wave * 256 + 4 * lane);
+          const uint32_t c = (f[0] ? 1u : 0u) + (f[1] ? 1u : 0u) + (f[2] ? 1u : 0u) + (f[3] ? 1u : 0u);
+          const uint32_t inc = wave_scan_dpp(c);
+          const uint32_t n = wave_bcast(inc, 63);
+          uint32_t o = inc - c;                                  // this lane's first staging slot
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], 0u));
-            if ((m[e] >> lane) & 1u) {
-              ck[pos + below] = key[e];
-              ci[pos + below] = jb + e;
+            if (f[e]) {
+              stage_k[o] = key[e];
+              stage_i[o] = jb + e;
             }
-            pos += (uint32_t)__popcll(m[e]);
+            o += f[e] ? 1u : 0u;
           }
+          for (uint32_t i = lane; i < n; i += 64) {
+            ck[pos + i] = stage_k[i];
+            ci[pos + i] = stage_i[i];
+          }
+          pos += n;
         }
       }
     }
@@ -560,16 +588,18 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
   if (!all) {
     const int lo = DC_BINS - 8 * (tid + 1);               // this thread's bins [lo, lo + 8)
     uint32_t hs[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    const uint32_t* src = a.shist + r * a.nsegs * (DC_BINS / 2) + lo / 2;
+    const uint32_t* src = a.shist + r * a.nsegs * (DC_BINS / 2) + (lo & 2047);
+    const int hsh = lo >= 2048 ? 16 : 0;
 #pragma unroll 4
     for (int sg = 0; sg < a.nsegs; ++sg) {
       // a sub-chunk without candidates has no keys (and a histogram that was never written)
-      const uint32_t keep = counts[sg] ? ~0u : 0u;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + (size_t)sg * (DC_BINS / 2));
+      const uint32_t keep = counts[sg] ? 0xFFFFu : 0u;
+      const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src + (size_t)sg * (DC_BINS / 2));
+      const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + (size_t)sg * (DC_BINS / 2) + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hs[2 * e] += v[e] & 0xFFFFu & keep;
-        hs[2 * e + 1] += (v[e] >> 16) & keep;
+        hs[e] += (v0[e] >> hsh) & keep;
+        hs[4 + e] += (v1[e] >> hsh) & keep;
       }
     }
     *reinterpret_cast<u32x4_t*>(hist + lo) = u32x4_t{hs[0], hs[1], hs[2], hs[3]};

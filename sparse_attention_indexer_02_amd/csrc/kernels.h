@@ -97,7 +97,8 @@ struct DecodeArgs {
                                    // dividing chunk)
   uint32_t* ccount;                // [B*T][nsegs] candidates per sub-chunk (written by the scan)
   uint32_t* shist;                 // [B*T][nsegs][DECODE_BINS / 2] each sub-chunk's first-digit
-                                   // histogram, bins 2w and 2w+1 in the halves of word w (scan)
+                                   // histogram: bins w and w + 2048 in the low and high 16-bit
+                                   // halves of word w (written by the scan)
   int nsegs;                       // sub-chunks per row: ceil(N / sub)
   uint32_t* cand_key; uint32_t* cand_idx;                    // [B*T][cand_cap] scan candidates
   uint32_t* cand2_key; uint32_t* cand2_idx;                  // [B*T][cand_cap] bin-b1 candidates
