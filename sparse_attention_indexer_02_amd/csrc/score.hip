@@ -209,8 +209,10 @@ score_kernel(ScoreArgs a) {
   int pbase = -1;                                     // first slot of the pending scores, or -1
 #pragma unroll
   for (int p = 0; p < NSUB / 2; ++p) pv[p] = 0.f;
+  // (a key list keeps the immediate stores: its registers are needed for the list indices)
+  constexpr bool DEFER = !LISTM;
   auto flush = [&]() {
-    if (pbase >= 0) {
+    if (DEFER && pbase >= 0) {
       if (fuse) {
 #pragma unroll
         for (int p = 0; p < NSUB / 2; ++p) {
@@ -327,7 +329,7 @@ score_kernel(ScoreArgs a) {
     } else {
       if (more) ld.store(tiles + (cur ^ 1) * G::TILE_BYTES, tid);
     }
-    if (full && !LISTM) {
+    if (DEFER && full) {
 #pragma unroll
       for (int p = 0; p < NSUB / 2; ++p) {
         const int n = p * 64 + lane;
