@@ -122,3 +122,16 @@ def test_decode_repeatable_sets():
         assert np.array_equal(np.take_along_axis(x[0], oa, -1), np.take_along_axis(y[0], ob, -1))
         assert np.array_equal(np.take_along_axis(x[1], oa, -1).view(np.uint32),
                               np.take_along_axis(y[1], ob, -1).view(np.uint32))
+
+
+def test_decode_many_segments_streaming_select():
+    # one sequence: the scan cuts the cache into ~1K-key sub-chunks, more than the selector's
+    # chunk table holds (64 segments), so the selector streams the candidates in batches
+    p = W.make_decode(1, 70000, T=2, seed=45)
+    say("case decode B=1 N=70000 (69 sub-chunks, streaming selector)")
+    gi, gs = run(p, 2048)
+    inp = oracle.Inputs(p)
+    for t in range(2):
+        r = oracle.dense_row(inp, 0, t, 2048)
+        check_selection(gi[0, t], gs[0, t], r["universe"], r["all_scores"], r["magnitude"],
+                        2048, p.D, ctx=f"decode-segments t{t}", oracle_sel=r["ids"])
