@@ -268,8 +268,8 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
     kernels = {name: idx.timer_read(name)
-               for name in ("score", "topk", "sort", "proxy", "pool", "block_refine", "decode_zero",
-                            "decode_scan", "decode_select", "decode_resolve")}
+               for name in ("score", "topk", "sort", "proxy", "pool", "block_refine", "decode_scan",
+                            "decode_select")}
     idx.timer_enable(False)
     log("[bench] per-kernel ms/step: " + ", ".join(
         f"{n} {ms / args.steps:.3f} ({c // max(1, args.steps)} launches)" for n, (ms, c) in kernels.items() if c))
