@@ -342,8 +342,14 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
     a.c0 = c0; a.c1 = c1;
     a.scores = pl.scores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
+    // bf16 rows shorter than 64K slots: each score-kernel wave selects its own row
+    const bool self_select = p->q_dtype == IDX_BF16 && p->k_dtype == IDX_BF16 && p->N < 65536;
+    if (self_select) {
+      a.sel_idx = out_idx; a.sel_score = out_score; a.sel_T = p->T;
+    }
     bool fused;
     if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s)))) return st;
+    if (fused && self_select) continue;
     TopkArgs t = topk_args(pl.scores, rstride(p->N), pl.row_len, p->B * (c1 - c0), k, c1 - c0, p->T, c0,
                            out_idx, out_score, k);
     t.row_meta = fused ? pl.meta : nullptr;

@@ -36,6 +36,9 @@ struct ScoreArgs {
   int rows_per_seq;                // score rows per sequence in this chunk
   int tiles_per_seq;
   int split_keys;                  // keys per grid.y split (multiple of the key tile)
+  // optional selection by the score kernel itself (key range, bf16, one key split, 12-bit
+  // summary): the top topk_k slots of row (b, t) go to sel_idx/sel_score [B, sel_T, topk_k]
+  int32_t* sel_idx; float* sel_score; int sel_T;
 };
 
 // Pick rows from per-row score arrays: the top-k slots of each row (a set; with a row summary

@@ -23,6 +23,226 @@ template <class Mma, int KST> struct TileKeys {
   static constexpr int value = Direct<Mma, KST>::value ? 128 : 64;
 };
 
+// One wave selects the top k slots of its own score row (n slots) from the row's 12-bit
+// first-digit summary: tot finite slots, bin b1 of the k-th largest key, `above` slots in higher
+// bins and `inbin` slots in bin b1. Pass 1 over the row writes the slots above bin b1 and keeps
+// the slots of bin b1: when they fit (inbin <= CAP) as (key, slot) pairs in LDS (keys in `ck`,
+// 16-bit slots in the upper half of `h`), otherwise as a histogram of their next 10 key bits. The
+// k-th key is then resolved digit by digit: 10 more bits give its 22-bit prefix; slots above the
+// prefix are written, and the slots sharing it (at most 256) are ranked exactly, higher key first,
+// then lower slot (ties keep the lowest slots); a prefix shared by more slots takes a last 10-bit
+// digit and keeps the lowest slots equal to the k-th key. Histograms use 1024 words of `h`. Without
+// the LDS copy the row is read again from global memory for each step. Row reads are eight
+// 16-byte loads per lane at a time. Output order: pass order, slot order within a pass.
+template <int CAP>
+__device__ __forceinline__ void wave_select_row(const float* srow, int n, int64_t stride, int k,
+                                                uint32_t tot, int b1, uint32_t above, uint32_t inbin,
+                                                uint32_t* h, uint32_t* ck, int32_t* oidx, float* osc) {
+  static_assert(CAP <= 2048, "16-bit slots in 1024 words");
+  constexpr int U = 8;
+  const int lane = lane_id();
+  const uint32_t kk = min((uint32_t)k, tot);
+  const bool all = kk == tot;
+  const bool gather = !all && inbin <= (uint32_t)CAP;
+  uint16_t* cs = reinterpret_cast<uint16_t*>(h + 1024);
+  const int last = (int)stride - 4;
+  // visits the row 256 slots at a time: f(i0, key[4], v) with key 0 past the row
+  auto stream = [&](auto f) {
+    for (int i0 = 0; i0 < n; i0 += 256 * U) {
+      f32x4_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = *reinterpret_cast<const f32x4_t*>(srow + min(i0 + 256 * u + 4 * lane, last));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j0 = i0 + 256 * u;
+        if (j0 >= n) break;
+        uint32_t key[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[e] = j0 + 4 * lane + e < n ? f2key(v[u][e]) : 0u;
+        f(j0, key, v[u]);
+      }
+    }
+  };
+  uint32_t pos = 0;
+  // writes the slots flagged in sel[4] at pos, in slot order
+  auto emit = [&](int i0, const bool (&sel)[4], const f32x4_t& v) {
+    const uint32_t c = (sel[0] ? 1u : 0u) + (sel[1] ? 1u : 0u) + (sel[2] ? 1u : 0u) + (sel[3] ? 1u : 0u);
+    const uint32_t inc = wave_scan_dpp(c);
+    uint32_t p = pos + inc - c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (sel[e]) {
+        oidx[p] = i0 + 4 * lane + e;
+        if (osc) osc[p] = v[e];
+      }
+      p += sel[e] ? 1u : 0u;
+    }
+    pos += wave_bcast(inc, 63);
+  };
+  // writes one flagged slot per lane at pos, in lane order
+  auto emit1 = [&](bool sel, uint32_t slot, uint32_t key) {
+    const uint32_t inc = wave_scan_dpp(sel ? 1u : 0u);
+    if (sel) {
+      oidx[pos + inc - 1] = (int32_t)slot;
+      if (osc) osc[pos + inc - 1] = key2f(key);
+    }
+    pos += wave_bcast(inc, 63);
+  };
+  auto zero_hist = [&] {
+    for (int i = lane; i < 1024; i += 64) h[i] = 0u;
+  };
+  // ranks the c2 (key, slot) pairs in h[0..256) / h[256..512) and writes the best `need`
+  auto rank_emit = [&](uint32_t c2, uint32_t need) {
+    for (int j0 = 0; j0 < (int)c2; j0 += 64) {
+      const int j = j0 + lane;
+      uint32_t kj = 0, sj = 0, r = 0;
+      if (j < (int)c2) {
+        kj = h[j];
+        sj = h[256 + j];
+        for (int i = 0; i < (int)c2; ++i) {
+          const uint32_t ki = h[i], si = h[256 + i];
+          r += (ki > kj || (ki == kj && si < sj)) ? 1u : 0u;
+        }
+      }
+      emit1(j < (int)c2 && r < need, sj, kj);
+    }
+  };
+  const uint32_t ub1 = (uint32_t)b1;
+  if (!all && !gather) zero_hist();
+  uint32_t cb = 0;                                       // gathered slots
+  stream([&](int i0, const uint32_t (&key)[4], const f32x4_t& v) {
+    bool sel[4];
+    uint32_t ce = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sel[e] = all ? key[e] > KEY_NEG_INF : (key[e] >> 20) > ub1;
+      ce += (key[e] >> 20) == ub1 ? 1u : 0u;
+    }
+    if (gather) {
+      const uint32_t einc = wave_scan_dpp(ce);
+      uint32_t p = cb + einc - ce;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((key[e] >> 20) == ub1 && p < (uint32_t)CAP) {   // p < inbin for finite keys
+          ck[p] = key[e];
+          cs[p] = (uint16_t)(i0 + 4 * lane + e);
+        }
+        p += (key[e] >> 20) == ub1 ? 1u : 0u;
+      }
+      cb += wave_bcast(einc, 63);
+    } else if (!all) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((key[e] >> 20) == ub1) atomicAdd(&h[(key[e] >> 10) & 0x3FFu], 1u);
+    }
+    emit(i0, sel, v);
+  });
+  if (!all) {
+    uint32_t need = kk - above;
+    int b2, b3;
+    uint32_t ab;
+    if (gather) {
+      zero_hist();
+      for (int i = lane; i < (int)inbin; i += 64) atomicAdd(&h[(ck[i] >> 10) & 0x3FFu], 1u);
+    }
+    wave_hist_find(1024, need, [&](int q) { return h[q]; }, &b2, &ab);
+    need -= ab;
+    const uint32_t pre = (ub1 << 10) | (uint32_t)b2;
+    const uint32_t c2 = h[b2];                           // slots sharing the 22-bit prefix
+    if (gather) {
+      if (c2 <= 256) {
+        uint32_t eb = 0;
+        for (int i0 = 0; i0 < (int)inbin; i0 += 64) {
+          const int i = i0 + lane;
+          const uint32_t key = i < (int)inbin ? ck[i] : 0u;
+          const uint32_t slot = i < (int)inbin ? cs[i] : 0u;
+          const bool eq = (key >> 10) == pre;
+          const uint32_t einc = wave_scan_dpp(eq ? 1u : 0u);
+          if (eq) {
+            h[eb + einc - 1] = key;
+            h[256 + eb + einc - 1] = slot;
+          }
+          eb += wave_bcast(einc, 63);
+          emit1((key >> 10) > pre, slot, key);
+        }
+        rank_emit(c2, need);
+      } else {
+        zero_hist();
+        for (int i = lane; i < (int)inbin; i += 64)
+          if ((ck[i] >> 10) == pre) atomicAdd(&h[ck[i] & 0x3FFu], 1u);
+        wave_hist_find(1024, need, [&](int q) { return h[q]; }, &b3, &ab);
+        const uint32_t T = (pre << 10) | (uint32_t)b3;
+        const uint32_t need_eq = need - ab;              // slots equal to T that are kept
+        uint32_t eqb = 0;
+        for (int i0 = 0; i0 < (int)inbin; i0 += 64) {
+          const int i = i0 + lane;
+          const uint32_t key = i < (int)inbin ? ck[i] : 0u;
+          const uint32_t slot = i < (int)inbin ? cs[i] : 0u;
+          const bool eq = key == T;
+          const uint32_t einc = wave_scan_dpp(eq ? 1u : 0u);
+          emit1(key > T || (eq && eqb + einc - 1 < need_eq), slot, key);
+          eqb += wave_bcast(einc, 63);
+        }
+      }
+    } else if (c2 <= 256) {
+      uint32_t eb = 0;
+      stream([&](int i0, const uint32_t (&key)[4], const f32x4_t& v) {
+        bool sel[4];
+        uint32_t ce = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sel[e] = (key[e] >> 20) == ub1 && (key[e] >> 10) > pre;
+          ce += (key[e] >> 10) == pre ? 1u : 0u;
+        }
+        const uint32_t einc = wave_scan_dpp(ce);
+        uint32_t p = eb + einc - ce;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((key[e] >> 10) == pre && p < 256u) {
+            h[p] = key[e];
+            h[256 + p] = (uint32_t)(i0 + 4 * lane + e);
+          }
+          p += (key[e] >> 10) == pre ? 1u : 0u;
+        }
+        eb += wave_bcast(einc, 63);
+        emit(i0, sel, v);
+      });
+      rank_emit(c2, need);
+    } else {
+      zero_hist();
+      stream([&](int, const uint32_t (&key)[4], const f32x4_t&) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((key[e] >> 10) == pre) atomicAdd(&h[key[e] & 0x3FFu], 1u);
+      });
+      wave_hist_find(1024, need, [&](int q) { return h[q]; }, &b3, &ab);
+      const uint32_t T = (pre << 10) | (uint32_t)b3;
+      const uint32_t need_eq = need - ab;                // slots equal to T that are kept
+      uint32_t eqb = 0;                                  // equal slots seen so far
+      stream([&](int i0, const uint32_t (&key)[4], const f32x4_t& v) {
+        const uint32_t ce = (key[0] == T ? 1u : 0u) + (key[1] == T ? 1u : 0u) + (key[2] == T ? 1u : 0u) +
+                            (key[3] == T ? 1u : 0u);
+        const uint32_t einc = wave_scan_dpp(ce);
+        uint32_t r = eqb + einc - ce;                    // rank of this lane's first equal slot
+        bool sel[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool eq = key[e] == T;
+          sel[e] = ((key[e] >> 20) == ub1 && key[e] > T) || (eq && r < need_eq);
+          r += eq ? 1u : 0u;
+        }
+        eqb += wave_bcast(einc, 63);
+        emit(i0, sel, v);
+      });
+    }
+  }
+  for (int p = (int)kk + lane; p < k; p += 64) {
+    oidx[p] = -1;
+    if (osc) osc[p] = -INFINITY;
+  }
+}
+
 template <class Mma, int D, int HB, int KST, bool LISTM>
 __global__ void __launch_bounds__(WavesFor<HB>::value * 64)
 score_kernel(ScoreArgs a) {
@@ -382,6 +602,19 @@ score_kernel(ScoreArgs a) {
       m[META_BIN] = bin;
       m[META_ABOVE] = (int32_t)above;
       m[META_INBIN] = bin >= 0 ? (int32_t)hist1_count(whist, bin, bits) : 0;
+    }
+    if constexpr (!LISTM) {
+      if (a.sel_idx != nullptr && bits == 12) {
+        wait_vmem();                                     // this wave's score stores
+        // the wave's share of the key tiles (idle after the last tile) holds bin b1's keys
+        constexpr int SLICE = 2 * G::TILE_BYTES / NW / 4;
+        const uint32_t inbin = bin >= 0 ? hist1_count(whist, bin, 12) : 0u;
+        wave_select_row<SLICE < 2048 ? SLICE : 2048>(
+            srow, my_count, a.score_stride, a.topk_k, tot, bin, above, inbin, whist,
+            reinterpret_cast<uint32_t*>(tiles + wave * (2 * G::TILE_BYTES / NW)),
+            a.sel_idx + ((int64_t)b * a.sel_T + t) * a.topk_k,
+                        a.sel_score ? a.sel_score + ((int64_t)b * a.sel_T + t) * a.topk_k : nullptr);
+      }
     }
   }
 }

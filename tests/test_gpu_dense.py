@@ -98,6 +98,37 @@ def test_degenerate_cases():
     assert (gi[1, 30:35, :31] >= 0).all()
 
 
+def test_exact_ties_keep_lowest_slots():
+    p = W.make_prefill(1500, 64, 128, seed=21)
+    p.k[0, 300:] = np.tile(p.k[0, :100], (12, 1))    # key 300 + 100 j + i repeats key i: equal scores
+    p.w[0, 1200:1210] = 0.0                          # rows whose every score is 0
+    k = 300
+    say("case exact ties: repeated keys and all-zero rows, L=1500 H=64 D=128 k=300")
+    gi, gs = run_dense(p, k)
+    check_rows(p, k, gi, gs, [(0, t) for t in list(range(280, 1500, 37)) + list(range(1200, 1210))], "ties")
+    for t in range(1200, 1210):                      # all scores 0: the k lowest tokens
+        assert set(gi[0, t].tolist()) == set(range(k)), f"ties t{t}"
+    for t in range(400, 1500):                       # a kept copy implies every lower copy is kept
+        sel = set(gi[0, t][gi[0, t] >= 0].tolist())
+        for s in sel:
+            if s >= 300:
+                lower = (s - 300) % 100 if s < 400 else s - 100
+                assert lower in sel, f"ties t{t}: token {s} kept but its lower copy {lower} not"
+
+
+def test_long_rows_wide_boundary_bin():
+    # D=64: the boundary bin of these rows holds more slots than the selector keeps on chip, so
+    # the selection reads the row again for each digit; the all-zero rows also tie at the k-th key
+    p = W.make_prefill(24000, 8, 64, seed=31)
+    p.w[0, 22000:22003] = 0.0
+    k = 2048
+    say("case long rows: L=24000 H=8 D=64 k=2048, three all-zero rows")
+    gi, gs = run_dense(p, k)
+    check_rows(p, k, gi, gs, [(0, t) for t in (2047, 2048, 9000, 17001, 22000, 22002, 23999)], "long")
+    for t in range(22000, 22003):
+        assert set(gi[0, t].tolist()) == set(range(k)), f"long t{t}"
+
+
 def test_deterministic():
     p = W.make_prefill(600, 64, 128, seed=12)
     say("case determinism")
