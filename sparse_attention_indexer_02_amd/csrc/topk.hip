@@ -382,6 +382,17 @@ __global__ void __launch_bounds__(64 * NWV) topk_reg_kernel(TopkArgs a) {
     const int32_t* lrow = gmode == MAP_LIST
         ? a.list + ((int64_t)bb * a.n_groups + tt / a.group_size) * a.list_stride : nullptr;
     const int32_t* brow = gmode == MAP_BLOCKS ? a.blocks + orow * a.blocks_stride : nullptr;
+    // with blocks of a multiple of 4 slots, a lane's 4 slots of step j share one block: its id is
+    // loaded for every step before the first output store (the compiler keeps a load after a
+    // store it cannot prove distinct, so loads between the stores would pay their latencies one
+    // after another)
+    const bool bk4 = gmode == MAP_BLOCKS && (a.block_size & 3) == 0;
+    int bk[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int i = w0 + 256 * j + 4 * lane;
+      bk[j] = bk4 && i < n ? brow[i / a.block_size] * a.block_size - i / a.block_size * a.block_size : 0;
+    }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       uint32_t gb = bg + (ex[j] & 0xFFFFu), eb = be + (ex[j] >> 16);
@@ -395,6 +406,7 @@ __global__ void __launch_bounds__(64 * NWV) topk_reg_kernel(TopkArgs a) {
           int key;
           if (gmode == MAP_IDENT) key = i;
           else if (gmode == MAP_LIST) key = lrow[i];
+          else if (bk4) key = bk[j] + i;
           else key = brow[i / a.block_size] * a.block_size + i % a.block_size;
           oidx[pos] = key;
           if (osc) osc[pos] = key2f(x);
@@ -653,9 +665,30 @@ __global__ void __launch_bounds__(TS_THREADS) topk_stream_kernel(TopkArgs a) {
   }
   __syncthreads();
   const int staged = min((int)kk, TS_OUT);
-  for (int p = tid; p < staged; p += TS_THREADS) {
-    oidx[p] = map_key(obi[p]);
-    if (osc) osc[p] = obs[p];
+  if constexpr (MAPM == MAP_IDENT) {
+    for (int p = tid; p < staged; p += TS_THREADS) {
+      oidx[p] = obi[p];
+      if (osc) osc[p] = obs[p];
+    }
+  } else {
+    // every mapped token of a thread is loaded before its first store (the compiler keeps a load
+    // after a store it cannot prove distinct, so interleaved loads would pay their latencies one
+    // after another)
+    constexpr int FL = (TS_OUT + TS_THREADS - 1) / TS_THREADS;
+    int fk[FL];
+#pragma unroll
+    for (int u = 0; u < FL; ++u) {
+      const int p = tid + u * TS_THREADS;
+      fk[u] = p < staged ? map_key(obi[p]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < FL; ++u) {
+      const int p = tid + u * TS_THREADS;
+      if (p < staged) {
+        oidx[p] = fk[u];
+        if (osc) osc[p] = obs[p];
+      }
+    }
   }
   for (int p = (int)kk + tid; p < a.k; p += TS_THREADS) {
     oidx[p] = -1;
@@ -776,8 +809,10 @@ hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s) {
   if (m <= 1024) hipLaunchKernelGGL((topk_reg_kernel<4, 1>), g, dim3(256), 0, s, a);
   else if (m <= 2048) hipLaunchKernelGGL((topk_reg_kernel<4, 2>), g, dim3(256), 0, s, a);
   else if (m <= 4096) hipLaunchKernelGGL((topk_reg_kernel<4, 4>), g, dim3(256), 0, s, a);
-  else if (m <= 8192) hipLaunchKernelGGL((topk_reg_kernel<4, 8>), g, dim3(256), 0, s, a);
-  else if (m <= 16384) hipLaunchKernelGGL((topk_reg_kernel<4, 16>), g, dim3(256), 0, s, a);
+  // rows of 4K-16K slots: 8 waves of 4 or 8 steps (16 resident waves per CU; 4 waves of 8 or 16
+  // steps need twice the registers per lane and leave 8)
+  else if (m <= 8192) hipLaunchKernelGGL((topk_reg_kernel<8, 4>), g, dim3(512), 0, s, a);
+  else if (m <= 16384) hipLaunchKernelGGL((topk_reg_kernel<8, 8>), g, dim3(512), 0, s, a);
   else if (m <= 32768) hipLaunchKernelGGL((topk_reg_kernel<8, 16>), g, dim3(512), 0, s, a);
   else hipLaunchKernelGGL(topk_long_kernel, g, dim3(TK_THREADS), 0, s, a);
   return hipGetLastError();
