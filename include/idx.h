@@ -56,7 +56,7 @@ enum {
 };
 
 /* operation ids for idx_workspace_bytes */
-enum { IDX_OP_SCORE_TOPK = 0, IDX_OP_GROUP = 1, IDX_OP_BLOCK = 2 };
+enum { IDX_OP_SCORE_TOPK = 0, IDX_OP_GROUP = 1, IDX_OP_BLOCK = 2, IDX_OP_REFINE = 3 };
 
 /* The indexer's inputs. Layouts are dense and row-major.
  *   q       [B, T, H, D]  q_dtype IDX_F32 or IDX_BF16
@@ -122,8 +122,31 @@ int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
                             int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
                             int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream);
 
+/* Per-query refine over candidate sets the caller supplies: a token bank shared by a group of
+ * queries and refined by each of them ("ADIndex: Layer-Adaptive Sparse Attention Indexing via
+ * Group-Level Distillation", abstract), or the candidate set an anchor layer proposes and a
+ * follower layer refines ("LatentIndex: Cross-Layer Sharing with Layer-Specific Selection for
+ * Sparse Attention", abstract, hierarchical selection).
+ * Queries are cut into groups of `group_size` consecutive queries (the last group may be
+ * shorter); group g of sequence b owns row (b, g) of `cand`:
+ *   cand     [B, ceil(T/group_size), n_cand] int32 (required): token ids; of each row the first
+ *            cand_cnt[b, g] entries are read (all n_cand when cand_cnt is NULL; counts are
+ *            clamped into [0, n_cand]);
+ *   cand_cnt [B, ceil(T/group_size)] int32 (optional).
+ * A row's candidate set is the set of the values read that are tokens of the sequence's cache,
+ * [0, k_len[b]): -1 padding and other values are dropped, repeated values count once. Every member then scores the
+ * candidates inside its own prefix with its own query and weights and keeps its top k (ties
+ * keep the lowest tokens), exactly as the refine step of idx_group_proxy_refine.
+ *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional).
+ * group_size = 1 gives each query its own set; a set holding the whole prefix gives
+ * idx_score_topk's result. Requires N <= 1048576 (IDX_ERR_UNSUPPORTED otherwise). */
+int idx_refine_given(const idx_problem* p, int32_t k, int32_t group_size, const int32_t* cand,
+                     const int32_t* cand_cnt, int32_t n_cand, int32_t* out_idx, float* out_score,
+                     void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes needed by one call. op = IDX_OP_*; p1, p2 = (group_size, n_cand) for
- * IDX_OP_GROUP, (block_size, n_blocks_keep) for IDX_OP_BLOCK, ignored for IDX_OP_SCORE_TOPK.
+ * IDX_OP_GROUP and IDX_OP_REFINE, (block_size, n_blocks_keep) for IDX_OP_BLOCK, ignored for
+ * IDX_OP_SCORE_TOPK.
  * Only the shape fields of *p are read (pointers may be NULL). Returns 0 for invalid arguments. */
 size_t idx_workspace_bytes(int op, const idx_problem* p, int32_t k, int32_t p1, int32_t p2);
 

@@ -8,6 +8,7 @@ error (there is no other implementation to fall back to).
     idx, score, cand = group_proxy_refine(q, k, w, q_pos, topk=2048, group_size=16, n_cand=8192)
     idx, score, blocks = block_coarse_refine(q, k, w, q_pos, topk=2048, block_size=128,
                                              n_blocks_keep=128)
+    idx, score = refine_given(q, k, w, q_pos, cand, cand_cnt=None, topk=2048, group_size=1)
 
 Shapes: q [B,T,H,D] (bf16 or fp32), k [B,N,D] (bf16, fp32, or float8_e4m3fn / uint8 E4M3FN
 bytes with k_scale [B,N] fp32), w [B,T,H] fp32, q_pos [B,T] int32, k_len [B] int32 or None.
@@ -23,13 +24,13 @@ from typing import Optional
 import torch
 
 __all__ = ["F32", "BF16", "FP8_E4M3", "IdxError", "lib", "score_topk", "group_proxy_refine",
-           "block_coarse_refine", "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
+           "block_coarse_refine", "refine_given", "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
-OP_SCORE_TOPK, OP_GROUP, OP_BLOCK = 0, 1, 2
+OP_SCORE_TOPK, OP_GROUP, OP_BLOCK, OP_REFINE = 0, 1, 2, 3
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidx.so")
 EXPORTS = ["idx_score_topk", "idx_group_proxy_refine", "idx_block_coarse_refine",
-           "idx_workspace_bytes", "idx_strerror", "idx_timer_enable", "idx_timer_read"]
+           "idx_refine_given", "idx_workspace_bytes", "idx_strerror", "idx_timer_enable", "idx_timer_read"]
 
 
 class IdxError(RuntimeError):
@@ -60,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.idx_score_topk.argtypes = [P, i32, vp, vp, vp, sz, vp]
         L.idx_group_proxy_refine.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.idx_block_coarse_refine.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.idx_refine_given.argtypes = [P, i32, i32, vp, vp, i32, vp, vp, vp, sz, vp]
         L.idx_workspace_bytes.argtypes = [ctypes.c_int, P, i32, i32, i32]
         L.idx_workspace_bytes.restype = sz
         L.idx_strerror.argtypes = [ctypes.c_int]
@@ -68,7 +70,7 @@ def lib() -> ctypes.CDLL:
         L.idx_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int32)]
         for f in ("idx_score_topk", "idx_group_proxy_refine", "idx_block_coarse_refine",
-                  "idx_timer_enable", "idx_timer_read"):
+                  "idx_refine_given", "idx_timer_enable", "idx_timer_read"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -186,6 +188,32 @@ def group_proxy_refine(q, k, w, q_pos, topk: int = 2048, group_size: int = 16,
                                         ws.numel() * ws.element_size(), _stream(q, stream)),
            "idx_group_proxy_refine")
     return out_idx, out_score, cand
+
+
+def refine_given(q, k, w, q_pos, cand, cand_cnt=None, topk: int = 2048, group_size: int = 1,
+                 k_len=None, k_scale=None, out_idx=None, out_score=None, want_score: bool = True,
+                 workspace=None, stream=None):
+    """Per-query refine over caller-supplied candidate sets (idx_refine_given).
+    cand: int32 [B, ceil(T/group_size), n_cand] token ids; cand_cnt: int32 [B, ceil(T/group_size)]
+    or None (all n_cand entries read). Values outside [0, k_len[b]) are dropped, repeats count
+    once."""
+    p = make_problem(q, k, w, q_pos, k_len, k_scale)
+    NG = (q.shape[1] + group_size - 1) // group_size
+    if cand.dtype != torch.int32 or cand.dim() != 3 or tuple(cand.shape[:2]) != (q.shape[0], NG):
+        raise IdxError(f"cand must be int32 [B, {NG}, n_cand]")
+    if cand_cnt is not None and (cand_cnt.dtype != torch.int32 or tuple(cand_cnt.shape) != (q.shape[0], NG)):
+        raise IdxError(f"cand_cnt must be int32 [B, {NG}]")
+    cand = cand.contiguous()
+    cand_cnt = cand_cnt.contiguous() if cand_cnt is not None else None
+    C = cand.shape[2]
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    need = workspace_bytes(OP_REFINE, p, topk, group_size, C)
+    ws = _workspace(q, need, workspace)
+    _check(lib().idx_refine_given(ctypes.byref(p), topk, group_size, _ptr(cand), _ptr(cand_cnt), C,
+                                  _ptr(out_idx), _ptr(out_score), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(q, stream)),
+           "idx_refine_given")
+    return out_idx, out_score
 
 
 def block_coarse_refine(q, k, w, q_pos, topk: int = 2048, block_size: int = 128,

@@ -132,6 +132,16 @@ DensePlan plan_dense(const idx_problem* p, void* ws) {
   return d;
 }
 
+struct RefinePlan {
+  int NG, chunkG;
+  int32_t* list;
+  int32_t* cnt;
+  float* mscores;
+  int32_t* row_len;
+  int32_t* meta;
+  size_t bytes;
+};
+
 struct GroupPlan {
   int NG, chunkP, chunkG;
   void* pq;
@@ -359,6 +369,36 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
   return IDX_OK;
 }
 
+// Per-query refine over per-group candidate lists (rows of C token ids in ascending order, the
+// first cnt[b * NG + g] used): members t of group g score the list's tokens inside their own
+// prefix (LIST mode of the score kernel) and keep their top k, mapped back to tokens.
+int refine_lists(const idx_problem* p, int32_t k, int G, int C, int NG, int chunkG, const int32_t* list,
+                 const int32_t* cnt, float* mscores, int32_t* row_len, int32_t* meta, int32_t* out_idx,
+                 float* out_score, hipStream_t s) {
+  int st;
+  for (int g0 = 0; g0 < NG; g0 += chunkG) {
+    const int g1 = std::min(NG, g0 + chunkG);
+    const int rows = std::min(p->T, g1 * G) - g0 * G;
+    ScoreArgs a = base_score_args(p);
+    a.mode = MODE_LIST;
+    a.list = list; a.list_len = cnt; a.list_stride = C; a.group_size = G;
+    a.n_groups = NG;
+    a.c0 = g0; a.c1 = g1;
+    a.scores = mscores; a.score_stride = rstride(C); a.row_len = row_len;
+    a.rows_per_seq = rows;
+    bool fused;
+    if ((st = from_hip(run_score(a, C, k, meta, &fused, s)))) return st;
+    TopkArgs t = topk_args(mscores, rstride(C), row_len, p->B * rows, k, rows, p->T, g0 * G, out_idx,
+                           out_score, k);
+    t.row_meta = fused ? meta : nullptr;
+    t.digit_bits = a.digit_bits;
+    t.map_mode = MAP_LIST;
+    t.list = list; t.list_stride = C; t.group_size = G; t.n_groups = NG;
+    if ((st = from_hip(run_topk(t, C, s)))) return st;
+  }
+  return IDX_OK;
+}
+
 int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* out_idx,
                float* out_score, int32_t* out_cand, void* ws, size_t ws_bytes, hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
@@ -397,28 +437,43 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
          return launch_sort_rows(pl.cand, C, pl.cand_cnt, p->B * pl.NG, C, p->N, s);
        }))))
     return st;
-  // per-member refine over the group's candidates
-  for (int g0 = 0; g0 < pl.NG; g0 += pl.chunkG) {
-    const int g1 = std::min(pl.NG, g0 + pl.chunkG);
-    const int rows = std::min(p->T, g1 * G) - g0 * G;
-    ScoreArgs a = base_score_args(p);
-    a.mode = MODE_LIST;
-    a.list = pl.cand; a.list_len = pl.cand_cnt; a.list_stride = C; a.group_size = G;
-    a.n_groups = pl.NG;
-    a.c0 = g0; a.c1 = g1;
-    a.scores = pl.mscores; a.score_stride = rstride(C); a.row_len = pl.row_len;
-    a.rows_per_seq = rows;
-    bool fused;
-    if ((st = from_hip(run_score(a, C, k, pl.meta, &fused, s)))) return st;
-    TopkArgs t = topk_args(pl.mscores, rstride(C), pl.row_len, p->B * rows, k, rows, p->T, g0 * G, out_idx,
-                           out_score, k);
-    t.row_meta = fused ? pl.meta : nullptr;
-    t.digit_bits = a.digit_bits;
-    t.map_mode = MAP_LIST;
-    t.list = pl.cand; t.list_stride = C; t.group_size = G; t.n_groups = pl.NG;
-    if ((st = from_hip(run_topk(t, C, s)))) return st;
-  }
-  return IDX_OK;
+  return refine_lists(p, k, G, C, pl.NG, pl.chunkG, pl.cand, pl.cand_cnt, pl.mscores, pl.row_len,
+                      pl.meta, out_idx, out_score, s);
+}
+
+RefinePlan plan_refine(const idx_problem* p, int G, int C, void* ws) {
+  RefinePlan g;
+  Carver c(ws);
+  g.NG = (p->T + G - 1) / G;
+  g.list = c.take<int32_t>((size_t)p->B * g.NG * C);
+  g.cnt = c.take<int32_t>((size_t)p->B * g.NG);
+  g.chunkG = chunk_rows(p->B, (int64_t)G * rstride(C) * 4, g.NG);
+  const int rows = std::min(p->T, g.chunkG * G);
+  g.mscores = c.take<float>((size_t)p->B * rows * rstride(C));
+  g.row_len = c.take<int32_t>((size_t)p->B * rows);
+  g.meta = c.take<int32_t>((size_t)p->B * rows * 4);
+  g.bytes = c.off + kAlign;
+  return g;
+}
+
+int refine_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, const int32_t* cand,
+                const int32_t* cand_cnt, int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                hipStream_t s) {
+  int st = validate(p, k, out_idx, out_score);
+  if (st) return st;
+  if (G < 1 || C < 1 || !cand) return IDX_ERR_INVALID_ARG;
+  if (!aligned(cand, 4) || (cand_cnt && !aligned(cand_cnt, 4))) return IDX_ERR_ALIGN;
+  if (p->N > 32768 * 32) return IDX_ERR_UNSUPPORTED;  // the set is built in an LDS bitmap of N bits
+  RefinePlan pl = plan_refine(p, G, C, nullptr);
+  if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
+  pl = plan_refine(p, G, C, align_ws(ws));
+  // the caller's lists as ascending sets of token ids (the refine indexes them by slot)
+  if ((st = from_hip(timed("sort", s, [&] {
+         return launch_given_lists(cand, cand_cnt, C, p->N, p->k_len, pl.NG, pl.list, pl.cnt, p->B * pl.NG, s);
+       }))))
+    return st;
+  return refine_lists(p, k, G, C, pl.NG, pl.chunkG, pl.list, pl.cnt, pl.mscores, pl.row_len, pl.meta,
+                      out_idx, out_score, s);
 }
 
 int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_t* out_idx,
@@ -526,6 +581,17 @@ int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
   }
 }
 
+int idx_refine_given(const idx_problem* p, int32_t k, int32_t group_size, const int32_t* cand,
+                     const int32_t* cand_cnt, int32_t n_cand, int32_t* out_idx, float* out_score,
+                     void* ws, size_t ws_bytes, void* stream) {
+  try {
+    return refine_impl(p, k, group_size, n_cand, cand, cand_cnt, out_idx, out_score, ws, ws_bytes,
+                       static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return IDX_ERR_INTERNAL;
+  }
+}
+
 size_t idx_workspace_bytes(int op, const idx_problem* p, int32_t k, int32_t p1, int32_t p2) {
   try {
     if (!p || p->B <= 0 || p->T <= 0 || p->H <= 0 || p->D <= 0 || p->N <= 0 || k <= 0) return 0;
@@ -538,6 +604,10 @@ size_t idx_workspace_bytes(int op, const idx_problem* p, int32_t k, int32_t p1, 
     if (op == IDX_OP_BLOCK) {
       if (p1 < 1 || p2 < 1) return 0;
       return plan_block(p, p1, p2, nullptr, nullptr).bytes;
+    }
+    if (op == IDX_OP_REFINE) {
+      if (p1 < 1 || p2 < 1) return 0;
+      return plan_refine(p, p1, p2, nullptr).bytes;
     }
   } catch (...) {
   }

@@ -114,6 +114,9 @@ hipError_t launch_score(const ScoreArgs& a, int n_splits, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+// caller-supplied candidate lists -> ascending sets of ids in [0, k_len[b]) (rows of C entries)
+hipError_t launch_given_lists(const int32_t* src, const int32_t* cnt, int C, int N, const int32_t* k_len,
+                              int n_groups, int32_t* dst, int32_t* dst_cnt, int n_rows, hipStream_t s);
 hipError_t launch_block_refine(const BlockRefineArgs& a, hipStream_t s);
 // Sorts rows of distinct values in [0, max_value) ascending (count[r] values in row r).
 hipError_t launch_sort_rows(int32_t* rows, int stride, const int32_t* count, int n_rows, int max_count,

@@ -11,6 +11,12 @@
 //   Attention", abstract, scores pooled block representations). Reading: the mean of the keys
 //   of each block of consecutive tokens that are in the cache, with the same fp32 order and
 //   rounding rule as the proxy, stored in the key format.
+//
+// given_lists_kernel: candidate sets supplied by the caller for a per-query refine ("ADIndex:
+//   Layer-Adaptive Sparse Attention Indexing via Group-Level Distillation", abstract: a token bank
+//   shared within a query group, refined per query; "LatentIndex: Cross-Layer Sharing with
+//   Layer-Specific Selection for Sparse Attention", abstract: followers refine the candidate set
+//   the anchor proposes). Each list becomes a set of token ids in ascending order.
 #include "common.h"
 #include "kernels.h"
 
@@ -151,6 +157,66 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((nb + per_wg - 1) / per_wg));
   if (a.k_dtype == DT_BF16) hipLaunchKernelGGL(pool_kernel<DT_BF16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(pool_kernel<DT_F32>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Row r = b * n_groups + g of `src` (C entries, the first cnt[r] of them used, all when cnt is
+// NULL; counts are clamped into [0, C]) becomes the ascending set of its values inside
+// [0, k_len[b]) (k_len NULL: [0, N)) in row r of `dst` (C entries), with the set's size in
+// dst_cnt[r]. Other values, such as -1 padding or tokens not in the cache, are dropped and
+// repeated values are kept once. One work-group per row: the values set bits of an
+// LDS bitmap of N bits, then each thread writes the set bits of its contiguous range of words at
+// the exclusive prefix of the popcounts.
+__global__ void __launch_bounds__(256) given_lists_kernel(const int32_t* src, const int32_t* cnt, int C,
+                                                          int N, const int32_t* k_len, int n_groups,
+                                                          int32_t* dst, int32_t* dst_cnt, int nwords) {
+  extern __shared__ uint32_t bm[];
+  __shared__ uint32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x;
+  const int32_t* row = src + (int64_t)r * C;
+  int32_t* out = dst + (int64_t)r * C;
+  const int c = cnt ? min(max(cnt[r], 0), C) : C;
+  const int kl = k_len ? max(0, min(k_len[r / n_groups], N)) : N;
+  for (int i = tid; i < nwords; i += 256) bm[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < c; i += 256) {
+    const int v = row[i];
+    if (v >= 0 && v < kl) atomicOr(&bm[v >> 5], 1u << (v & 31));
+  }
+  __syncthreads();
+  const int per = (nwords + 255) / 256;
+  const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
+  uint32_t n = 0;
+  for (int w = w0; w < w1; ++w) n += __popc(bm[w]);
+  const uint32_t inc = wave_scan_dpp(n);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t pos = inc - n;
+  for (int w = 0; w < wave; ++w) pos += wsum[w];
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = bm[w];
+    while (m) {
+      out[pos++] = w * 32 + __builtin_ctz(m);
+      m &= m - 1u;
+    }
+  }
+  if (tid == 0) dst_cnt[r] = (int32_t)(wsum[0] + wsum[1] + wsum[2] + wsum[3]);
+}
+
+hipError_t launch_given_lists(const int32_t* src, const int32_t* cnt, int C, int N, const int32_t* k_len,
+                              int n_groups, int32_t* dst, int32_t* dst_cnt, int n_rows, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  const int nwords = (N + 31) / 32;
+  if (nwords > 32768) return hipErrorInvalidValue;   // the bitmap must fit in LDS (128 KB)
+  const size_t lds = (size_t)nwords * sizeof(uint32_t);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(given_lists_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(given_lists_kernel, dim3(n_rows), dim3(256), lds, s, src, cnt, C, N, k_len, n_groups,
+                     dst, dst_cnt, nwords);
   return hipGetLastError();
 }
 

@@ -112,6 +112,18 @@ def test_variant_arguments(L):
     assert b(16, 4, fp8) == -2
 
 
+def test_refine_given_arguments(L):
+    p = _problem()
+    r = lambda G, cand, C, pp=p, ws_bytes=1 << 40: L.idx_refine_given(
+        ctypes.byref(pp), 8, G, cand, None, C, 0x50000, None, 0x60000, ws_bytes, None)
+    assert r(0, 0x70000, 16) == -1 and r(4, None, 16) == -1 and r(4, 0x70000, 0) == -1
+    assert r(4, 0x70002, 16) == -3                                   # candidates not 4-aligned
+    assert r(4, 0x70000, 16, pp=_problem(N=1048577)) == -2           # set bitmap beyond LDS
+    assert r(4, 0x70000, 16, ws_bytes=100) == -4
+    assert L.idx_workspace_bytes(idx.OP_REFINE, ctypes.byref(p), 8, 4, 16) > 0
+    assert L.idx_workspace_bytes(idx.OP_REFINE, ctypes.byref(p), 8, 4, 0) == 0
+
+
 def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 4, 2, 32, dtype=torch.bfloat16)

@@ -1,0 +1,111 @@
+"""GPU parity of the per-query refine over caller-supplied candidate sets (idx_refine_given)
+against the oracle's refine step: per-query sets with padding, repeats and out-of-range ids, a
+group-shared token bank with FP8 keys, the whole prefix (equal to the dense indexer), and the
+group path's own candidate lists (equal to the group path's output)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import sparse_attention_indexer_02_amd as idx
+from gpu_util import dev, say
+from parity import check_selection
+
+pytestmark = pytest.mark.gpu
+
+
+def run_given(prob, k, G, cand, cnt=None):
+    t = dev(prob)
+    c = torch.from_numpy(np.ascontiguousarray(cand, np.int32)).cuda()
+    n = torch.from_numpy(np.ascontiguousarray(cnt, np.int32)).cuda() if cnt is not None else None
+    oi, osc = idx.refine_given(t["q"], t["k"], t["w"], t["q_pos"], c, cand_cnt=n, topk=k,
+                               group_size=G, k_len=t["k_len"], k_scale=t["k_scale"])
+    torch.cuda.synchronize()
+    return oi.cpu().numpy(), osc.cpu().numpy()
+
+
+def given_set(row, cnt, N):
+    """The candidate set the entry point defines for one row: the distinct values among the
+    first cnt entries that are tokens of the cache, [0, k_len)."""
+    v = np.asarray(row[:cnt], np.int64)
+    return np.unique(v[(v >= 0) & (v < N)])
+
+
+def check_rows(prob, k, G, cand, cnt, gi, gs, rows, name):
+    inp = oracle.Inputs(prob)
+    C = cand.shape[2]
+    for b, t in rows:
+        g = t // G
+        n = C if cnt is None else int(np.clip(cnt[b, g], 0, C))
+        r = oracle.refine_row(inp, b, t, k, given_set(cand[b, g], n, int(prob.k_len[b])))
+        check_selection(gi[b, t], gs[b, t], r["universe"], r["all_scores"], r["magnitude"], k,
+                        prob.D, ctx=f"{name} b{b} t{t}", oracle_sel=r["ids"])
+
+
+def test_per_query_sets_with_padding_repeats_and_out_of_range():
+    p = W.make_prefill(400, 64, 128, seed=41)
+    rng = np.random.default_rng(41)
+    C, k = 120, 48
+    cand = np.full((1, p.T, C), -1, np.int32)
+    cnt = np.zeros((1, p.T), np.int32)
+    for t in range(p.T):
+        m = int(rng.integers(0, C + 1))
+        v = rng.integers(0, p.N, m)                       # some beyond the query's prefix
+        v[rng.random(m) < 0.1] = -1                       # padding inside the counted part
+        v[rng.random(m) < 0.05] = p.N + 7                 # out of range
+        if m > 2:
+            v[-1] = v[0]                                  # a repeat
+        cand[0, t, :m] = v
+        cnt[0, t] = m if t % 7 else C + 5                 # some counts above n_cand (clamped)
+    say("case refine_given: L=400 H=64 D=128, per-query sets of up to 120, k=48")
+    gi, gs = run_given(p, k, 1, cand, cnt)
+    check_rows(p, k, 1, cand, cnt, gi, gs, [(0, t) for t in range(p.T)], "given-per-query")
+
+
+def test_group_bank_fp8_keys_ragged_batch():
+    p = W.make_prefill(300, 16, 64, seed=42, B=2, k_dtype=W.FP8_E4M3)
+    p.k_len[1] = 250
+    rng = np.random.default_rng(42)
+    G, C, k = 16, 96, 40
+    NG = (p.T + G - 1) // G
+    cand = np.stack([np.stack([rng.permutation(p.N)[:C] for _ in range(NG)]) for _ in range(p.B)])
+    say("case refine_given: B=2 L=300 fp8 keys, banks of 96 shared by 16 queries, k=40")
+    gi, gs = run_given(p, k, G, cand.astype(np.int32))
+    check_rows(p, k, G, cand, None, gi, gs, [(b, t) for b in range(p.B) for t in range(p.T)],
+               "given-bank")
+
+
+def test_whole_prefix_equals_dense():
+    p = W.make_prefill(257, 32, 128, seed=43)
+    k = 64
+    cand = np.broadcast_to(np.arange(p.N, dtype=np.int32)[::-1], (1, p.T, p.N)).copy()
+    say("case refine_given: every query's set is the whole cache (reversed order)")
+    gi, gs = run_given(p, k, 1, cand)
+    inp = oracle.Inputs(p)
+    for t in range(p.T):
+        r = oracle.dense_row(inp, 0, t, k)
+        check_selection(gi[0, t], gs[0, t], r["universe"], r["all_scores"], r["magnitude"], k,
+                        p.D, ctx=f"given-dense t{t}", oracle_sel=r["ids"])
+
+
+def test_group_candidates_reproduce_group_path():
+    p = W.make_prefill(4096, 64, 128, seed=44, rho=0.95)
+    G, C, k = 16, 1024, 256
+    t = dev(p)
+    say("case refine_given vs group path: L=4096 G=16 C=1024 k=256")
+    oi, osc, cand = idx.group_proxy_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
+                                           group_size=G, n_cand=C, return_cand=True)
+    ri, rs = idx.refine_given(t["q"], t["k"], t["w"], t["q_pos"], cand, topk=k, group_size=G)
+    torch.cuda.synchronize()
+    oi, osc, ri, rs = (x.cpu().numpy() for x in (oi, osc, ri, rs))
+    # the same candidate sets through the same refine: identical sets and scores per row
+    for tt in range(p.T):
+        a = np.argsort(oi[0, tt])
+        c = np.argsort(ri[0, tt])
+        assert np.array_equal(oi[0, tt][a], ri[0, tt][c]), f"row {tt}"
+        assert np.array_equal(osc[0, tt][a].view(np.uint32), rs[0, tt][c].view(np.uint32)), f"row {tt}"
+    gc = cand.cpu().numpy()
+    rng = np.random.default_rng(44)
+    check_rows(p, k, G, gc, None, ri, rs, [(0, int(x)) for x in [0, 15, 16, 4095] + list(rng.integers(0, 4096, 6))],
+               "given-group")
