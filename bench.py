@@ -124,6 +124,20 @@ def group_refine_pairs(prob, G, C):
     return proxy, refine
 
 
+def given_pairs(prob, G, banks):
+    """Pairs scored by the refine over given banks: each member's bank tokens inside its prefix."""
+    import numpy as np
+    n = 0
+    for b in range(prob.B):
+        for g in range(banks.shape[1]):
+            v = np.unique(banks[b, g])
+            v = v[v >= 0]
+            for t in range(g * G, min(prob.T, g * G + G)):
+                P = min(int(prob.q_pos[b, t]) + 1, int(prob.k_len[b]))
+                n += int(np.searchsorted(v, P))
+    return n
+
+
 def block_pairs(prob, Bs, keep):
     import numpy as np
     pos = prob.q_pos[0].astype(np.int64)
@@ -139,6 +153,7 @@ def cpu_oracle_baseline(name, spec, prob, budget_s=12.0):
     """Times the oracle on a bounded, evenly spaced row sample of the workload."""
     import numpy as np
     import oracle
+    import workloads as W
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()
@@ -176,6 +191,18 @@ def cpu_oracle_baseline(name, spec, prob, budget_s=12.0):
             if time.perf_counter() - t0 > budget_s:
                 break
         sample = f"{rows} query rows of {T} in whole groups, interleaved with stride {stride} (proxy scan + refine)"
+    elif op == "given":
+        G = spec["group_size"]
+        banks = W.make_banks(prob, G, spec["n_cand"], 0)
+        stride = max(1, T // 128)
+        for t in [t for off in range(stride) for t in range(T - 1 - off, -1, -stride)]:
+            v = banks[0, t // G]
+            oracle.refine_row(inp, 0, t, spec["k"], np.unique(v[v >= 0]))
+            done_pairs += inp.P(0, t)
+            rows += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = f"{rows} query rows of {T} (interleaved with stride {stride}), refine over the given bank"
     else:
         Bs, keep = spec["block_size"], spec["n_blocks_keep"]
         pooled = oracle.pool_keys(prob, 0, Bs)
@@ -231,6 +258,10 @@ def main():
         need = idx.workspace_bytes(idx.OP_SCORE_TOPK, p, k)
     elif op == "group":
         need = idx.workspace_bytes(idx.OP_GROUP, p, k, spec["group_size"], spec["n_cand"])
+    elif op == "given":
+        banks_np = W.make_banks(prob, spec["group_size"], spec["n_cand"], args.seed)
+        banks = torch.from_numpy(banks_np).to("cuda:0")
+        need = idx.workspace_bytes(idx.OP_REFINE, p, k, spec["group_size"], spec["n_cand"])
     else:
         need = idx.workspace_bytes(idx.OP_BLOCK, p, k, spec["block_size"], spec["n_blocks_keep"])
     ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
@@ -244,6 +275,10 @@ def main():
                                    group_size=spec["group_size"], n_cand=spec["n_cand"],
                                    k_len=t["k_len"], k_scale=t["k_scale"], out_idx=out_idx,
                                    out_score=out_sc, workspace=ws)
+        elif op == "given":
+            idx.refine_given(t["q"], t["k"], t["w"], t["q_pos"], banks, topk=k,
+                             group_size=spec["group_size"], k_len=t["k_len"], k_scale=t["k_scale"],
+                             out_idx=out_idx, out_score=out_sc, workspace=ws)
         else:
             idx.block_coarse_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
                                     block_size=spec["block_size"],
@@ -310,6 +345,16 @@ def main():
                 "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
         cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"],
                    algorithmic_pairs_per_step=pp + rp)
+    elif op == "given":
+        rp = given_pairs(prob, spec["group_size"], banks_np)
+        ms, n = kernels["score"]
+        flops = 2.0 * prob.H * prob.D * rp
+        achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(args.workload, "score_kernel"),
+                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
+        cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"], algorithmic_pairs_per_step=rp)
     else:
         cp, rp = block_pairs(prob, spec["block_size"], spec["n_blocks_keep"])
         ms, n = kernels["block_refine"]

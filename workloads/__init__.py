@@ -199,6 +199,24 @@ def make_hier(N, T, H=64, D=128, *, seed=0, rho=0.9, n_regions=64, region=128,
     return Problem(qs, BF16, ks, BF16, None, w, q_pos, np.array([N], np.int32))
 
 
+def make_banks(prob: Problem, G: int, C: int, seed: int = 0) -> np.ndarray:
+    """Candidate token banks for a per-query refine over caller-supplied sets: for each group of
+    G consecutive queries, C distinct tokens drawn uniformly from the group's prefix (the tokens
+    up to the largest member position that are in the cache), in random order, -1 padded when the
+    prefix is shorter than C. int32 [B, ceil(T/G), C]."""
+    rng = np.random.default_rng(seed + 1000)
+    B, T = prob.q_pos.shape
+    NG = (T + G - 1) // G
+    out = np.full((B, NG, C), -1, np.int32)
+    for b in range(B):
+        for g in range(NG):
+            pos = int(prob.q_pos[b, g * G:min(T, g * G + G)].max())
+            P = max(0, min(pos + 1, int(prob.k_len[b])))
+            m = min(C, P)
+            out[b, g, :m] = rng.choice(P, m, replace=False)
+    return out
+
+
 # ----------------------------------------------------------------------------------------------
 # named workloads (the five shapes the indexer pages' long-context experiments suggest)
 
@@ -212,6 +230,8 @@ WORKLOADS = {
                        gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed)),
     "group64k": dict(op="group", k=2048, group_size=16, n_cand=8192,
                      gen=lambda seed=0: make_prefill(65536, 64, 128, seed=seed, rho=0.95)),
+    "given16k": dict(op="given", k=2048, group_size=16, n_cand=4096,
+                     gen=lambda seed=0: make_prefill(16384, 64, 128, seed=seed, rho=0.9)),
     "hier128k": dict(op="block", k=2048, block_size=128, n_blocks_keep=128,
                      gen=lambda seed=0: make_hier(131072, 4096, seed=seed)),
 }
