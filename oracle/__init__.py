@@ -264,6 +264,39 @@ def group(prob, k: int, G: int, n_cand: int):
     return out_idx, out_sc, cands
 
 
+def reuse_row(inp: Inputs, b: int, t: int, ps):
+    """PIVOT-Reuse ([PIVOT]: the proxy's top-k is shared across the group, nothing is re-scored).
+    `ps` is group_proxy_scan with n_cand = k, so its candidates are the proxy's top-k. Reading:
+    a member keeps the proxy's top-k tokens that lie in its own causal prefix (an earlier member
+    sees a shorter prefix than the proxy), each with the proxy's score. Returns dict(ids, scores)
+    in the proxy's rank order."""
+    P = inp.P(b, t)
+    ids = np.asarray(ps["cand_by_rank"], np.int64)
+    keep = ids < P
+    return dict(ids=ids[keep], scores=ps["proxy_scores"][ids[keep]])
+
+
+def group_reuse(prob, k: int, G: int):
+    """Full PIVOT-Reuse output: (out_idx [B,T,k] int32 -1 padded, out_score -inf padded, proxy
+    scans {(b,g): group_proxy_scan(..., n_cand=k)})."""
+    inp = Inputs(prob)
+    B, T = prob.q_pos.shape
+    NG = (T + G - 1) // G
+    out_idx = np.full((B, T, k), -1, np.int32)
+    out_sc = np.full((B, T, k), -np.inf)
+    scans = {}
+    for b in range(B):
+        for g in range(NG):
+            ps = group_proxy_scan(inp, b, g, G, k)
+            scans[(b, g)] = ps
+            for t in group_members(T, G, g):
+                r = reuse_row(inp, b, t, ps)
+                n = len(r["ids"])
+                out_idx[b, t, :n] = r["ids"]
+                out_sc[b, t, :n] = r["scores"]
+    return out_idx, out_sc, scans
+
+
 # ----------------------------------------------------------------------------------------------
 # block-pooled coarse filter with token refine  [HISA]
 

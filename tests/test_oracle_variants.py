@@ -83,6 +83,36 @@ def test_group_outputs_within_candidates(pre):
         assert len(sel) == min(k, len(vis))
 
 
+def test_reuse_singletons_equal_dense(pre):
+    # G=1: the proxy is the query itself (mean of one value, bf16 of a bf16 value), so sharing
+    # its top-k is the dense indexer, scores included
+    k = 24
+    d_idx, d_sc = oracle.dense(pre, k)
+    r_idx, r_sc, _ = oracle.group_reuse(pre, k, 1)
+    assert np.array_equal(r_idx, d_idx)
+    assert np.array_equal(r_sc, d_sc)
+
+
+def test_reuse_members_share_the_proxy_topk(pre):
+    k, G = 16, 8
+    r_idx, r_sc, scans = oracle.group_reuse(pre, k, G)
+    inp = oracle.Inputs(pre)
+    for (b, g), ps in scans.items():
+        mem = list(oracle.group_members(pre.T, G, g))
+        top = ps["cand_by_rank"]
+        assert len(top) == min(k, ps["P"])
+        # the proxy's top-k over its own prefix, ties to the lower token
+        ref, _ = oracle.select_topk(ps["proxy_scores"], np.arange(ps["P"]), k)
+        assert np.array_equal(top, ref)
+        last = max(mem, key=lambda t: pre.q_pos[b, t])
+        assert np.array_equal(r_idx[b, last, :len(top)], top)       # the furthest member: all of it
+        for t in mem:                                              # the others: its part in their prefix
+            sel = r_idx[b, t][r_idx[b, t] >= 0]
+            assert np.array_equal(sel, top[top < inp.P(b, t)])
+            assert np.array_equal(r_sc[b, t, :len(sel)], ps["proxy_scores"][sel])
+            assert (r_idx[b, t, len(sel):] == -1).all()
+
+
 def test_group_partial_last_group():
     p = W.make_prefill(37, 2, 16, seed=3)
     _, _, cands = oracle.group(p, 8, 16, 20)
