@@ -191,6 +191,19 @@ def cpu_oracle_baseline(name, spec, prob, budget_s=12.0):
             if time.perf_counter() - t0 > budget_s:
                 break
         sample = f"{rows} query rows of {T} in whole groups, interleaved with stride {stride} (proxy scan + refine)"
+    elif op == "reuse":
+        G = spec["group_size"]
+        NG = (T + G - 1) // G
+        stride = max(1, NG // 64)
+        for g in [g for off in range(stride) for g in range(NG - 1 - off, -1, -stride)]:
+            ps = oracle.group_proxy_scan(inp, 0, g, G, spec["k"])
+            for t in oracle.group_members(T, G, g):
+                oracle.reuse_row(inp, 0, t, ps)
+                done_pairs += inp.P(0, t)
+                rows += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = f"{rows} query rows of {T} in whole groups, interleaved with stride {stride} (proxy scan + reuse)"
     elif op == "given":
         G = spec["group_size"]
         banks = W.make_banks(prob, G, spec["n_cand"], 0)
@@ -258,6 +271,8 @@ def main():
         need = idx.workspace_bytes(idx.OP_SCORE_TOPK, p, k)
     elif op == "group":
         need = idx.workspace_bytes(idx.OP_GROUP, p, k, spec["group_size"], spec["n_cand"])
+    elif op == "reuse":
+        need = idx.workspace_bytes(idx.OP_REUSE, p, k, spec["group_size"], 0)
     elif op == "given":
         banks_np = W.make_banks(prob, spec["group_size"], spec["n_cand"], args.seed)
         banks = torch.from_numpy(banks_np).to("cuda:0")
@@ -275,6 +290,11 @@ def main():
                                    group_size=spec["group_size"], n_cand=spec["n_cand"],
                                    k_len=t["k_len"], k_scale=t["k_scale"], out_idx=out_idx,
                                    out_score=out_sc, workspace=ws)
+        elif op == "reuse":
+            idx.group_proxy_reuse(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
+                                  group_size=spec["group_size"], k_len=t["k_len"],
+                                  k_scale=t["k_scale"], out_idx=out_idx, out_score=out_sc,
+                                  workspace=ws)
         elif op == "given":
             idx.refine_given(t["q"], t["k"], t["w"], t["q_pos"], banks, topk=k,
                              group_size=spec["group_size"], k_len=t["k_len"], k_scale=t["k_scale"],
@@ -303,8 +323,8 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
     kernels = {name: idx.timer_read(name)
-               for name in ("score", "topk", "sort", "proxy", "pool", "block_refine", "decode_scan",
-                            "decode_select")}
+               for name in ("score", "topk", "sort", "proxy", "pool", "block_refine", "reuse",
+                            "decode_scan", "decode_select")}
     idx.timer_enable(False)
     log("[bench] per-kernel ms/step: " + ", ".join(
         f"{n} {ms / args.steps:.3f} ({c // max(1, args.steps)} launches)" for n, (ms, c) in kernels.items() if c))
@@ -345,6 +365,16 @@ def main():
                 "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
         cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"],
                    algorithmic_pairs_per_step=pp + rp)
+    elif op == "reuse":
+        pp, _ = group_refine_pairs(prob, spec["group_size"], 1)
+        ms, n = kernels["score"]
+        flops = 2.0 * prob.H * prob.D * pp
+        achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(args.workload, "score_kernel"),
+                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
+        cfg.update(group_size=spec["group_size"], algorithmic_pairs_per_step=pp)
     elif op == "given":
         rp = given_pairs(prob, spec["group_size"], banks_np)
         ms, n = kernels["score"]

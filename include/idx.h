@@ -56,7 +56,7 @@ enum {
 };
 
 /* operation ids for idx_workspace_bytes */
-enum { IDX_OP_SCORE_TOPK = 0, IDX_OP_GROUP = 1, IDX_OP_BLOCK = 2, IDX_OP_REFINE = 3 };
+enum { IDX_OP_SCORE_TOPK = 0, IDX_OP_GROUP = 1, IDX_OP_BLOCK = 2, IDX_OP_REFINE = 3, IDX_OP_REUSE = 4 };
 
 /* The indexer's inputs. Layouts are dense and row-major.
  *   q       [B, T, H, D]  q_dtype IDX_F32 or IDX_BF16
@@ -101,7 +101,9 @@ int idx_score_topk(const idx_problem* p, int32_t k, int32_t* out_idx, float* out
  *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
  *   out_cand [B, ceil(T/group_size), n_cand] int32 (optional): each group's candidates in
  *            ascending token order, -1 padded.
- * With n_cand >= the prefix length the result equals idx_score_topk's. Requires n_cand <= N. */
+ * With n_cand >= the prefix length the result equals idx_score_topk's. Requires n_cand <= N.
+ * In decode, a group is the queries decoded together in one multi-token-prediction step (same
+ * abstract): pass group_size = T, the number of MTP queries per sequence. */
 int idx_group_proxy_refine(const idx_problem* p, int32_t k, int32_t group_size, int32_t n_cand,
                            int32_t* out_idx, float* out_score, int32_t* out_cand,
                            void* ws, size_t ws_bytes, void* stream);
@@ -121,6 +123,17 @@ int idx_group_proxy_refine(const idx_problem* p, int32_t k, int32_t group_size, 
 int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
                             int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
                             int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream);
+
+/* Group-shared scan without refine ("PIVOT ...", abstract; PIVOT-Reuse: the proxy's top-k is
+ * shared across the group). Groups and proxies are those of idx_group_proxy_refine. The proxy
+ * scores its prefix once and keeps its k best tokens (ties to the lower token); every member
+ * takes those of them inside its own prefix, with the proxy's scores, and nothing is re-scored.
+ * The member with the largest position receives the whole proxy top-k; group_size = 1 gives
+ * idx_score_topk's result. In decode, group_size = T groups one step's MTP queries.
+ *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional): the member's part
+ *           of the proxy top-k (order unspecified), then -1 / -inf. */
+int idx_group_proxy_reuse(const idx_problem* p, int32_t k, int32_t group_size, int32_t* out_idx,
+                          float* out_score, void* ws, size_t ws_bytes, void* stream);
 
 /* Per-query refine over candidate sets the caller supplies: a token bank shared by a group of
  * queries and refined by each of them ("ADIndex: Layer-Adaptive Sparse Attention Indexing via
@@ -145,8 +158,8 @@ int idx_refine_given(const idx_problem* p, int32_t k, int32_t group_size, const 
                      void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by one call. op = IDX_OP_*; p1, p2 = (group_size, n_cand) for
- * IDX_OP_GROUP and IDX_OP_REFINE, (block_size, n_blocks_keep) for IDX_OP_BLOCK, ignored for
- * IDX_OP_SCORE_TOPK.
+ * IDX_OP_GROUP and IDX_OP_REFINE, (block_size, n_blocks_keep) for IDX_OP_BLOCK, (group_size,
+ * ignored) for IDX_OP_REUSE, ignored for IDX_OP_SCORE_TOPK.
  * Only the shape fields of *p are read (pointers may be NULL). Returns 0 for invalid arguments. */
 size_t idx_workspace_bytes(int op, const idx_problem* p, int32_t k, int32_t p1, int32_t p2);
 
@@ -157,7 +170,8 @@ const char* idx_strerror(int status);
  * records a HIP event pair around each kernel launch on the call's stream. idx_timer_read
  * waits for the recorded events and returns the summed milliseconds and the launch count of
  * the kernels whose name contains `kernel_substr` (all kernels if NULL or ""); kernel names are
- * "score", "topk", "sort", "proxy", "pool", "block_refine", "decode_scan" and "decode_select".
+ * "score", "topk", "sort", "proxy", "pool", "block_refine", "reuse", "decode_scan" and
+ * "decode_select".
  * idx_timer_enable(on) clears the record
  * and switches recording on or off. Not thread safe. */
 int idx_timer_enable(int on);

@@ -132,6 +132,20 @@ DensePlan plan_dense(const idx_problem* p, void* ws) {
   return d;
 }
 
+struct ReusePlan {
+  int NG, chunkP;
+  void* pq;
+  float* pw;
+  int32_t* ppos;
+  float* pscores;
+  int32_t* gidx;
+  float* gsc;
+  int32_t* gcnt;
+  int32_t* row_len;
+  int32_t* meta;
+  size_t bytes;
+};
+
 struct RefinePlan {
   int NG, chunkG;
   int32_t* list;
@@ -441,6 +455,65 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
                       pl.meta, out_idx, out_score, s);
 }
 
+ReusePlan plan_reuse(const idx_problem* p, int G, int k, void* ws) {
+  ReusePlan g;
+  Carver c(ws);
+  g.NG = (p->T + G - 1) / G;
+  const size_t qeb = p->q_dtype == IDX_BF16 ? 2 : 4;
+  g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
+  g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
+  g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
+  g.chunkP = chunk_rows(p->B, rstride(p->N) * 4, g.NG);
+  g.pscores = c.take<float>((size_t)p->B * g.chunkP * rstride(p->N));
+  g.gidx = c.take<int32_t>((size_t)p->B * g.NG * k);
+  g.gsc = c.take<float>((size_t)p->B * g.NG * k);
+  g.gcnt = c.take<int32_t>((size_t)p->B * g.NG);
+  g.row_len = c.take<int32_t>((size_t)p->B * g.chunkP);
+  g.meta = c.take<int32_t>((size_t)p->B * g.chunkP * 4);
+  g.bytes = c.off + kAlign;
+  return g;
+}
+
+// PIVOT-Reuse: the proxies' prefix scans keep each group's top k (tokens and proxy scores), and
+// every member takes the part of it inside its own prefix.
+int reuse_impl(const idx_problem* p, int32_t k, int32_t G, int32_t* out_idx, float* out_score,
+               void* ws, size_t ws_bytes, hipStream_t s) {
+  int st = validate(p, k, out_idx, out_score);
+  if (st) return st;
+  if (G < 1) return IDX_ERR_INVALID_ARG;
+  ReusePlan pl = plan_reuse(p, G, k, nullptr);
+  if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
+  pl = plan_reuse(p, G, k, align_ws(ws));
+
+  ProxyArgs pa;
+  pa.q = p->q; pa.q_dtype = p->q_dtype; pa.w = p->w; pa.q_pos = p->q_pos;
+  pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.D = p->D; pa.G = G; pa.n_groups = pl.NG;
+  pa.pq = pl.pq; pa.pw = pl.pw; pa.ppos = pl.ppos;
+  if ((st = from_hip(timed("proxy", s, [&] { return launch_proxy(pa, s); })))) return st;
+  for (int c0 = 0; c0 < pl.NG; c0 += pl.chunkP) {
+    const int c1 = std::min(pl.NG, c0 + pl.chunkP);
+    ScoreArgs a = base_score_args(p);
+    a.q = pl.pq; a.w = pl.pw; a.q_pos = pl.ppos; a.T = pl.NG;
+    a.c0 = c0; a.c1 = c1;
+    a.scores = pl.pscores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
+    a.rows_per_seq = c1 - c0;
+    bool fused;
+    if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s)))) return st;
+    TopkArgs t = topk_args(pl.pscores, rstride(p->N), pl.row_len, p->B * (c1 - c0), k, c1 - c0, pl.NG, c0,
+                           pl.gidx, pl.gsc, k);
+    t.out_count = pl.gcnt;
+    t.row_meta = fused ? pl.meta : nullptr;
+    t.digit_bits = a.digit_bits;
+    if ((st = from_hip(run_topk(t, p->N, s)))) return st;
+  }
+  ReuseArgs r;
+  r.gidx = pl.gidx; r.gsc = pl.gsc; r.gcnt = pl.gcnt;
+  r.q_pos = p->q_pos; r.k_len = p->k_len;
+  r.B = p->B; r.T = p->T; r.N = p->N; r.G = G; r.NG = pl.NG; r.k = k;
+  r.out_idx = out_idx; r.out_score = out_score;
+  return from_hip(timed("reuse", s, [&] { return launch_reuse_rows(r, s); }));
+}
+
 RefinePlan plan_refine(const idx_problem* p, int G, int C, void* ws) {
   RefinePlan g;
   Carver c(ws);
@@ -581,6 +654,16 @@ int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
   }
 }
 
+int idx_group_proxy_reuse(const idx_problem* p, int32_t k, int32_t group_size, int32_t* out_idx,
+                          float* out_score, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    return reuse_impl(p, k, group_size, out_idx, out_score, ws, ws_bytes,
+                      static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return IDX_ERR_INTERNAL;
+  }
+}
+
 int idx_refine_given(const idx_problem* p, int32_t k, int32_t group_size, const int32_t* cand,
                      const int32_t* cand_cnt, int32_t n_cand, int32_t* out_idx, float* out_score,
                      void* ws, size_t ws_bytes, void* stream) {
@@ -604,6 +687,10 @@ size_t idx_workspace_bytes(int op, const idx_problem* p, int32_t k, int32_t p1, 
     if (op == IDX_OP_BLOCK) {
       if (p1 < 1 || p2 < 1) return 0;
       return plan_block(p, p1, p2, nullptr, nullptr).bytes;
+    }
+    if (op == IDX_OP_REUSE) {
+      if (p1 < 1) return 0;
+      return plan_reuse(p, p1, k, nullptr).bytes;
     }
     if (op == IDX_OP_REFINE) {
       if (p1 < 1 || p2 < 1) return 0;

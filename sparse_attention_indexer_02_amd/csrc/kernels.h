@@ -70,6 +70,13 @@ struct ProxyArgs {
   void* pq; float* pw; int32_t* ppos;   // [B, NG, H, D], [B, NG, H], [B, NG]
 };
 
+struct ReuseArgs {
+  const int32_t* gidx; const float* gsc; const int32_t* gcnt;   // [B, NG, k], [B, NG, k], [B, NG]
+  const int32_t* q_pos; const int32_t* k_len;
+  int B, T, N, G, NG, k;
+  int32_t* out_idx; float* out_score;                           // [B, T, k]
+};
+
 struct PoolArgs {
   const void* keys; int k_dtype; const int32_t* k_len;
   int B, N, D, block_size, n_blocks;    // n_blocks = ceil(N / block_size) (row capacity)
@@ -114,6 +121,7 @@ hipError_t launch_score(const ScoreArgs& a, int n_splits, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+hipError_t launch_reuse_rows(const ReuseArgs& a, hipStream_t s);
 // caller-supplied candidate lists -> ascending sets of ids in [0, k_len[b]) (rows of C entries)
 hipError_t launch_given_lists(const int32_t* src, const int32_t* cnt, int C, int N, const int32_t* k_len,
                               int n_groups, int32_t* dst, int32_t* dst_cnt, int n_rows, hipStream_t s);

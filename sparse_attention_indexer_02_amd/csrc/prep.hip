@@ -17,6 +17,10 @@
 //   shared within a query group, refined per query; "LatentIndex: Cross-Layer Sharing with
 //   Layer-Specific Selection for Sparse Attention", abstract: followers refine the candidate set
 //   the anchor proposes). Each list becomes a set of token ids in ascending order.
+//
+// reuse_rows_kernel: PIVOT-Reuse ("PIVOT ...", abstract: the proxy's top-k is shared across the
+//   group). Reading: each member keeps the proxy's top-k tokens inside its own causal prefix,
+//   with the proxy's scores.
 #include "common.h"
 #include "kernels.h"
 
@@ -202,6 +206,60 @@ __global__ void __launch_bounds__(256) given_lists_kernel(const int32_t* src, co
     }
   }
   if (tid == 0) dst_cnt[r] = (int32_t)(wsum[0] + wsum[1] + wsum[2] + wsum[3]);
+}
+
+// One wave per member row (b, t) of group g = t / G: the first gcnt[b * NG + g] entries of the
+// group's top-k row (gidx, gsc: [B, NG, k]) that lie in the member's prefix
+// [0, min(q_pos + 1, k_len)) go to out_idx / out_score row (b, t) in the group's order; the rest
+// of the row is -1 / -inf.
+__global__ void __launch_bounds__(256) reuse_rows_kernel(ReuseArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.B * a.T) return;                 // whole wave
+  const int b = (int)(row / a.T), t = (int)(row % a.T), g = t / a.G;
+  const int kl = a.k_len ? max(0, min(a.k_len[b], a.N)) : a.N;
+  const int P = max(0, min(a.q_pos[row] + 1, kl));
+  const int64_t src = ((int64_t)b * a.NG + g) * a.k;
+  const int n = min(max(a.gcnt[(int64_t)b * a.NG + g], 0), a.k);
+  int32_t* oi = a.out_idx + row * a.k;
+  float* os = a.out_score ? a.out_score + row * a.k : nullptr;
+  // eight 64-entry steps are loaded before their stores (the compiler keeps a load behind a
+  // store it cannot prove distinct, so per-step loads would pay their latencies one by one)
+  constexpr int U = 8;
+  int pos = 0;
+  for (int i0 = 0; i0 < n; i0 += 64 * U) {
+    int v[U];
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 64 * u + lane;
+      v[u] = i < n ? a.gidx[src + i] : -1;
+      sc[u] = i < n ? a.gsc[src + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool keep = v[u] >= 0 && v[u] < P;
+      const uint64_t m = __ballot(keep);
+      if (keep) {
+        const int p = pos + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        oi[p] = v[u];
+        if (os) os[p] = sc[u];
+      }
+      pos += __popcll(m);
+    }
+  }
+  for (int p = pos + lane; p < a.k; p += 64) {
+    oi[p] = -1;
+    if (os) os[p] = -INFINITY;
+  }
+}
+
+hipError_t launch_reuse_rows(const ReuseArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.T;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reuse_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_given_lists(const int32_t* src, const int32_t* cnt, int C, int N, const int32_t* k_len,

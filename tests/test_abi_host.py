@@ -124,6 +124,15 @@ def test_refine_given_arguments(L):
     assert L.idx_workspace_bytes(idx.OP_REFINE, ctypes.byref(p), 8, 4, 0) == 0
 
 
+def test_reuse_arguments(L):
+    p = _problem()
+    u = lambda G, ws_bytes=1 << 40: L.idx_group_proxy_reuse(ctypes.byref(p), 8, G, 0x50000, None,
+                                                            0x60000, ws_bytes, None)
+    assert u(0) == -1 and u(4, ws_bytes=100) == -4
+    assert L.idx_workspace_bytes(idx.OP_REUSE, ctypes.byref(p), 8, 4, 0) > 0
+    assert L.idx_workspace_bytes(idx.OP_REUSE, ctypes.byref(p), 8, 0, 0) == 0
+
+
 def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 4, 2, 32, dtype=torch.bfloat16)

@@ -1,0 +1,78 @@
+"""GPU parity of PIVOT-Reuse (idx_group_proxy_reuse) against the oracle, and of decode-phase
+grouping (a group = one step's multi-token-prediction queries) for both PIVOT variants. The
+proxy top-k is compared where it is unique (tie band at the k-th proxy score) on the member that
+receives all of it; every other member must hold exactly its part inside the member's prefix,
+with the same scores bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import sparse_attention_indexer_02_amd as idx
+from gpu_util import dev, say
+from parity import check_selection
+from test_gpu_variants import run_group, check_group
+
+pytestmark = pytest.mark.gpu
+
+
+def run_reuse(prob, k, G):
+    t = dev(prob)
+    oi, osc = idx.group_proxy_reuse(t["q"], t["k"], t["w"], t["q_pos"], topk=k, group_size=G,
+                                    k_len=t["k_len"], k_scale=t["k_scale"])
+    torch.cuda.synchronize()
+    return oi.cpu().numpy(), osc.cpu().numpy()
+
+
+def check_reuse(prob, k, G, gi, gs, name):
+    inp = oracle.Inputs(prob)
+    NG = (prob.T + G - 1) // G
+    for b in range(prob.B):
+        for g in range(NG):
+            mem = list(oracle.group_members(prob.T, G, g))
+            ps = oracle.group_proxy_scan(inp, b, g, G, k)
+            far = max(mem, key=lambda t: prob.q_pos[b, t])
+            check_selection(gi[b, far], gs[b, far], np.arange(ps["P"]), ps["proxy_scores"],
+                            ps["proxy_magnitude"], k, prob.D, ctx=f"{name} b{b} g{g} t{far}",
+                            oracle_sel=ps["cand"])
+            top = gi[b, far][gi[b, far] >= 0]
+            sc = dict(zip(top.tolist(), gs[b, far][gi[b, far] >= 0].view(np.uint32).tolist()))
+            for t in mem:
+                sel = gi[b, t][gi[b, t] >= 0]
+                want = top[top < inp.P(b, t)]
+                assert set(sel.tolist()) == set(want.tolist()), f"{name} b{b} t{t}"
+                assert len(sel) == len(want) and (gi[b, t, len(sel):] == -1).all()
+                got = gs[b, t][: len(sel)].view(np.uint32).tolist()
+                assert got == [sc[v] for v in sel.tolist()], f"{name} b{b} t{t} scores"
+                assert np.isneginf(gs[b, t, len(sel):]).all()
+
+
+def test_reuse_singletons_equal_dense():
+    p = W.make_prefill(300, 64, 128, seed=51)
+    k = 40
+    say("case reuse G=1: L=300 H=64 D=128 k=40 (must equal the dense indexer)")
+    gi, gs = run_reuse(p, k, 1)
+    inp = oracle.Inputs(p)
+    for t in range(p.T):
+        r = oracle.dense_row(inp, 0, t, k)
+        check_selection(gi[0, t], gs[0, t], r["universe"], r["all_scores"], r["magnitude"], k,
+                        p.D, ctx=f"reuse-1 t{t}", oracle_sel=r["ids"])
+
+
+def test_reuse_prefill_groups_and_ragged_batch():
+    p = W.make_prefill(700, 64, 128, seed=52, B=2, rho=0.95)
+    p.k_len[1] = 500
+    say("case reuse G=16: B=2 L=700 (k_len 500 for b1) k=48")
+    gi, gs = run_reuse(p, 48, 16)
+    check_reuse(p, 48, 16, gi, gs, "reuse-16")
+
+
+def test_decode_grouping_fp8_both_variants():
+    p = W.make_decode(3, 6000, T=2, seed=53, k_len=[6000, 4321, 100])
+    G, k, C = 2, 256, 1024
+    say("case decode grouping: B=3 N=6000 T=2 fp8, G=T=2; reuse k=256, refine C=1024")
+    gi, gs = run_reuse(p, k, G)
+    check_reuse(p, k, G, gi, gs, "decode-reuse")
+    ri, rs, rc = run_group(p, k, G, C)
+    check_group(p, k, G, C, ri, rs, rc, [(b, 0) for b in range(p.B)], "decode-refine")

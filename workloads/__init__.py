@@ -230,6 +230,8 @@ WORKLOADS = {
                        gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed)),
     "group64k": dict(op="group", k=2048, group_size=16, n_cand=8192,
                      gen=lambda seed=0: make_prefill(65536, 64, 128, seed=seed, rho=0.95)),
+    "reuse64k": dict(op="reuse", k=2048, group_size=16,
+                     gen=lambda seed=0: make_prefill(65536, 64, 128, seed=seed, rho=0.95)),
     "given16k": dict(op="given", k=2048, group_size=16, n_cand=4096,
                      gen=lambda seed=0: make_prefill(16384, 64, 128, seed=seed, rho=0.9)),
     "hier128k": dict(op="block", k=2048, block_size=128, n_blocks_keep=128,
