@@ -76,3 +76,17 @@ def test_decode_grouping_fp8_both_variants():
     check_reuse(p, k, G, gi, gs, "decode-reuse")
     ri, rs, rc = run_group(p, k, G, C)
     check_group(p, k, G, C, ri, rs, rc, [(b, 0) for b in range(p.B)], "decode-refine")
+
+
+def test_reuse_long_proxy_rows_and_ties():
+    # ten proxies over prefixes of up to 40000 keys: too few rows for one work-group per row
+    # range, so the proxy rows come without a summary and take the long-row selector; one group
+    # has all-zero head weights (every proxy score 0: ties keep the lowest tokens)
+    p = W.make_prefill(40000, 8, 64, seed=54)
+    G, k = 4096, 2048
+    p.w[0, 2 * G:3 * G] = 0.0
+    say("case reuse long proxy rows: L=40000 H=8 D=64 G=4096 k=2048, one all-zero group")
+    gi, gs = run_reuse(p, k, G)
+    check_reuse(p, k, G, gi, gs, "reuse-long")
+    far = 3 * G - 1
+    assert set(gi[0, far].tolist()) == set(range(k)), "ties: lowest tokens"
