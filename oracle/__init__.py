@@ -352,6 +352,50 @@ def block_row(inp: Inputs, b: int, t: int, k: int, block_size: int, n_keep: int,
     return r
 
 
+def group_block_scan(inp: Inputs, b: int, g: int, G: int, block_size: int, n_keep: int,
+                     pooled: np.ndarray):
+    """The block-filtered proxy (PIVOT's group proxy ([PIVOT]) scoring HISA's pooled blocks
+    ([HISA]) instead of every token of its prefix). Reading: the proxy of proxy_query scores the
+    pooled blocks whose first token is in its prefix and keeps the min(n_keep, eligible) best
+    (ties to the lower block); the group's candidates are the tokens of the kept blocks.
+    Returns dict(blocks ascending, block_scores, block_magnitude, tokens ascending)."""
+    prob = inp.prob
+    qb, wb, pos = proxy_query(prob, b, g, G)
+    q64 = queries_f64(qb, prob.q_dtype)
+    w64 = wb.astype(np.float64)
+    pk = pooled.astype(np.float64) if prob.k_dtype == F32 else bf16_bits_to_f64(pooled)
+    NB = pk.shape[0]
+    n_elig = 0 if pos < 0 else min(NB, pos // block_size + 1)
+    bs = index_scores(q64, w64, pk[:n_elig])
+    kept, _ = select_topk(bs, np.arange(n_elig, dtype=np.int64), n_keep)
+    kept = np.sort(kept)
+    toks = (kept[:, None] * block_size + np.arange(block_size)[None]).reshape(-1)
+    toks = toks[toks < int(prob.k_len[b])]
+    return dict(blocks=kept, block_scores=bs, block_magnitude=score_magnitude(q64, w64, pk[:n_elig]),
+                tokens=toks)
+
+
+def group_block(prob, k: int, G: int, block_size: int, n_keep: int):
+    """Block-filtered proxy with per-query refine: (out_idx [B,T,k], out_score, scans {(b,g)})."""
+    inp = Inputs(prob)
+    B, T = prob.q_pos.shape
+    NG = (T + G - 1) // G
+    out_idx = np.full((B, T, k), -1, np.int32)
+    out_sc = np.full((B, T, k), -np.inf)
+    scans = {}
+    for b in range(B):
+        pooled = pool_keys(prob, b, block_size)
+        for g in range(NG):
+            gs = group_block_scan(inp, b, g, G, block_size, n_keep, pooled)
+            scans[(b, g)] = gs
+            for t in group_members(T, G, g):
+                r = refine_row(inp, b, t, k, gs["tokens"])
+                n = len(r["ids"])
+                out_idx[b, t, :n] = r["ids"]
+                out_sc[b, t, :n] = r["scores"]
+    return out_idx, out_sc, scans
+
+
 def block(prob, k: int, block_size: int, n_keep: int):
     """Full hierarchical output: (out_idx, out_score, blocks [B,T,n_keep] padded with -1)."""
     inp = Inputs(prob)

@@ -195,3 +195,36 @@ def test_block_outputs_within_kept_blocks(hier):
         sel = b_idx[0, t][b_idx[0, t] >= 0]
         assert set((sel // bs).tolist()) <= set(kept.tolist())
         assert sel.max() <= hier.q_pos[0, t]
+
+
+# -------------------------------------------------------------------------- block-filtered proxy
+
+def test_group_block_singletons_equal_block(hier):
+    # G=1: the proxy is the query itself, so the result is the hierarchical indexer's
+    k, Bs, keep = 16, 8, 5
+    b_idx, b_sc = oracle.block(hier, k, Bs, keep)[:2]
+    g_idx, g_sc, _ = oracle.group_block(hier, k, 1, Bs, keep)
+    assert np.array_equal(g_idx, b_idx)
+    assert np.array_equal(g_sc, b_sc)
+
+
+def test_group_block_keep_all_equals_dense(hier):
+    # every eligible block kept: the candidates hold each member's whole prefix
+    k = 16
+    d_idx, d_sc = oracle.dense(hier, k)
+    for G in (1, 6):
+        g_idx, g_sc, _ = oracle.group_block(hier, k, G, 8, 10 ** 6)
+        for t in range(hier.T):
+            assert set(g_idx[0, t].tolist()) == set(d_idx[0, t].tolist())
+        assert np.array_equal(np.sort(g_sc, -1), np.sort(d_sc, -1))
+
+
+def test_group_block_candidates_are_kept_blocks(hier):
+    k, G, Bs, keep = 12, 4, 8, 3
+    g_idx, _, scans = oracle.group_block(hier, k, G, Bs, keep)
+    for (b, g), gs in scans.items():
+        assert len(gs["blocks"]) == min(keep, len(gs["block_scores"]))
+        assert set((gs["tokens"] // Bs).tolist()) == set(gs["blocks"].tolist())
+        for t in oracle.group_members(hier.T, G, g):
+            sel = g_idx[b, t][g_idx[b, t] >= 0]
+            assert set(sel.tolist()) <= set(gs["tokens"].tolist())
