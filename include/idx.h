@@ -135,6 +135,27 @@ int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
 int idx_group_proxy_reuse(const idx_problem* p, int32_t k, int32_t group_size, int32_t* out_idx,
                           float* out_score, void* ws, size_t ws_bytes, void* stream);
 
+/* Block-filtered group proxy: the group proxy of idx_group_proxy_refine ("PIVOT ...", abstract)
+ * scores the pooled blocks of idx_block_coarse_refine ("HISA ...", abstract) instead of every
+ * token of its prefix. Each group's proxy scores the pooled blocks whose first token is in its
+ * prefix and keeps its n_blocks_keep best (ties to the lower block); every member then scores
+ * the tokens of the kept blocks inside its own prefix with its own query and weights and keeps
+ * its top k.
+ *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
+ *   out_blocks [B, ceil(T/group_size), n_blocks_keep] int32 (optional): each group's kept blocks
+ *              in ascending order, -1 padded.
+ * Keys must be IDX_BF16 or IDX_F32. Requires ceil(N / block_size) <= 65536 and
+ * n_blocks_keep <= 32767. group_size = 1 gives idx_block_coarse_refine's result; keeping every
+ * block gives idx_score_topk's. Its workspace size is idx_group_block_workspace_bytes(...). */
+int idx_group_block_refine(const idx_problem* p, int32_t k, int32_t group_size, int32_t block_size,
+                           int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
+                           int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of idx_group_block_refine for the same arguments (only the shape fields of *p
+ * are read); 0 for invalid arguments. */
+size_t idx_group_block_workspace_bytes(const idx_problem* p, int32_t k, int32_t group_size,
+                                       int32_t block_size, int32_t n_blocks_keep);
+
 /* Per-query refine over candidate sets the caller supplies: a token bank shared by a group of
  * queries and refined by each of them ("ADIndex: Layer-Adaptive Sparse Attention Indexing via
  * Group-Level Distillation", abstract), or the candidate set an anchor layer proposes and a

@@ -10,6 +10,8 @@ error (there is no other implementation to fall back to).
                                              n_blocks_keep=128)
     idx, score = refine_given(q, k, w, q_pos, cand, cand_cnt=None, topk=2048, group_size=1)
     idx, score = group_proxy_reuse(q, k, w, q_pos, topk=2048, group_size=16)
+    idx, score, blocks = group_block_refine(q, k, w, q_pos, topk=2048, group_size=16,
+                                            block_size=128, n_blocks_keep=128)
 
 Shapes: q [B,T,H,D] (bf16 or fp32), k [B,N,D] (bf16, fp32, or float8_e4m3fn / uint8 E4M3FN
 bytes with k_scale [B,N] fp32), w [B,T,H] fp32, q_pos [B,T] int32, k_len [B] int32 or None.
@@ -25,13 +27,14 @@ from typing import Optional
 import torch
 
 __all__ = ["F32", "BF16", "FP8_E4M3", "IdxError", "lib", "score_topk", "group_proxy_refine",
-           "block_coarse_refine", "refine_given", "group_proxy_reuse", "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
+           "block_coarse_refine", "refine_given", "group_proxy_reuse", "group_block_refine", "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OP_SCORE_TOPK, OP_GROUP, OP_BLOCK, OP_REFINE, OP_REUSE = 0, 1, 2, 3, 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidx.so")
 EXPORTS = ["idx_score_topk", "idx_group_proxy_refine", "idx_block_coarse_refine",
-           "idx_refine_given", "idx_group_proxy_reuse", "idx_workspace_bytes", "idx_strerror", "idx_timer_enable", "idx_timer_read"]
+           "idx_refine_given", "idx_group_proxy_reuse", "idx_group_block_refine",
+           "idx_group_block_workspace_bytes", "idx_workspace_bytes", "idx_strerror", "idx_timer_enable", "idx_timer_read"]
 
 
 class IdxError(RuntimeError):
@@ -64,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.idx_block_coarse_refine.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.idx_refine_given.argtypes = [P, i32, i32, vp, vp, i32, vp, vp, vp, sz, vp]
         L.idx_group_proxy_reuse.argtypes = [P, i32, i32, vp, vp, vp, sz, vp]
+        L.idx_group_block_refine.argtypes = [P, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.idx_group_block_workspace_bytes.argtypes = [P, i32, i32, i32, i32]
+        L.idx_group_block_workspace_bytes.restype = sz
         L.idx_workspace_bytes.argtypes = [ctypes.c_int, P, i32, i32, i32]
         L.idx_workspace_bytes.restype = sz
         L.idx_strerror.argtypes = [ctypes.c_int]
@@ -72,7 +78,8 @@ def lib() -> ctypes.CDLL:
         L.idx_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int32)]
         for f in ("idx_score_topk", "idx_group_proxy_refine", "idx_block_coarse_refine",
-                  "idx_refine_given", "idx_group_proxy_reuse", "idx_timer_enable", "idx_timer_read"):
+                  "idx_refine_given", "idx_group_proxy_reuse", "idx_group_block_refine",
+                  "idx_timer_enable", "idx_timer_read"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -205,6 +212,27 @@ def group_proxy_reuse(q, k, w, q_pos, topk: int = 2048, group_size: int = 16, k_
                                        _stream(q, stream)),
            "idx_group_proxy_reuse")
     return out_idx, out_score
+
+
+def group_block_refine(q, k, w, q_pos, topk: int = 2048, group_size: int = 16,
+                       block_size: int = 128, n_blocks_keep: int = 128, k_len=None, k_scale=None,
+                       out_idx=None, out_score=None, want_score: bool = True,
+                       return_blocks: bool = False, workspace=None, stream=None):
+    """Block-filtered group proxy with per-query refine (idx_group_block_refine)."""
+    p = make_problem(q, k, w, q_pos, k_len, k_scale)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    blocks = None
+    if return_blocks:
+        NG = (q.shape[1] + group_size - 1) // group_size
+        blocks = torch.empty((q.shape[0], NG, n_blocks_keep), dtype=torch.int32, device=q.device)
+    need = int(lib().idx_group_block_workspace_bytes(ctypes.byref(p), topk, group_size, block_size,
+                                                     n_blocks_keep))
+    ws = _workspace(q, need, workspace)
+    _check(lib().idx_group_block_refine(ctypes.byref(p), topk, group_size, block_size, n_blocks_keep,
+                                        _ptr(out_idx), _ptr(out_score), _ptr(blocks), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(q, stream)),
+           "idx_group_block_refine")
+    return out_idx, out_score, blocks
 
 
 def refine_given(q, k, w, q_pos, cand, cand_cnt=None, topk: int = 2048, group_size: int = 1,

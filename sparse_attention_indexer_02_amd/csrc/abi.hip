@@ -146,6 +146,23 @@ struct ReusePlan {
   size_t bytes;
 };
 
+struct GroupBlockPlan {
+  int NG, NB, chunkP, chunkG;
+  void* pq;
+  float* pw;
+  int32_t* ppos;
+  void* pooled;
+  float* cscores;
+  int32_t* blocks;
+  int32_t* n_kept;
+  int32_t* list;
+  int32_t* cnt;
+  float* mscores;
+  int32_t* row_len;
+  int32_t* meta;
+  size_t bytes;
+};
+
 struct RefinePlan {
   int NG, chunkG;
   int32_t* list;
@@ -514,6 +531,93 @@ int reuse_impl(const idx_problem* p, int32_t k, int32_t G, int32_t* out_idx, flo
   return from_hip(timed("reuse", s, [&] { return launch_reuse_rows(r, s); }));
 }
 
+GroupBlockPlan plan_group_block(const idx_problem* p, int G, int Bs, int keep, void* ws,
+                                int32_t* out_blocks) {
+  GroupBlockPlan g;
+  Carver c(ws);
+  g.NG = (p->T + G - 1) / G;
+  g.NB = (p->N + Bs - 1) / Bs;
+  const int C = keep * Bs;
+  const size_t qeb = p->q_dtype == IDX_BF16 ? 2 : 4;
+  const size_t keb = p->k_dtype == IDX_BF16 ? 2 : 4;
+  g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
+  g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
+  g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
+  g.pooled = c.take<uint8_t>((size_t)p->B * g.NB * p->D * keb);
+  g.chunkP = chunk_rows(p->B, rstride(g.NB) * 4, g.NG);
+  g.cscores = c.take<float>((size_t)p->B * g.chunkP * rstride(g.NB));
+  g.blocks = out_blocks ? out_blocks : c.take<int32_t>((size_t)p->B * g.NG * keep);
+  g.n_kept = c.take<int32_t>((size_t)p->B * g.NG);
+  g.list = c.take<int32_t>((size_t)p->B * g.NG * C);
+  g.cnt = c.take<int32_t>((size_t)p->B * g.NG);
+  g.chunkG = chunk_rows(p->B, (int64_t)G * rstride(C) * 4, g.NG);
+  const int rows = std::max(std::min(p->T, g.chunkG * G), g.chunkP);
+  g.mscores = c.take<float>((size_t)p->B * std::min(p->T, g.chunkG * G) * rstride(C));
+  g.row_len = c.take<int32_t>((size_t)p->B * rows);
+  g.meta = c.take<int32_t>((size_t)p->B * rows * 4);
+  g.bytes = c.off + kAlign;
+  return g;
+}
+
+// Block-filtered group proxy: each group's proxy scores the pooled blocks of its prefix and
+// keeps `keep` of them; every member refines the tokens of the kept blocks.
+int group_block_impl(const idx_problem* p, int32_t k, int32_t G, int32_t Bs, int32_t keep,
+                     int32_t* out_idx, float* out_score, int32_t* out_blocks, void* ws, size_t ws_bytes,
+                     hipStream_t s) {
+  int st = validate(p, k, out_idx, out_score);
+  if (st) return st;
+  if (G < 1 || Bs < 1 || keep < 1) return IDX_ERR_INVALID_ARG;
+  if (p->k_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;
+  if ((p->N + (int64_t)Bs - 1) / Bs > 65536 || keep > 32767) return IDX_ERR_UNSUPPORTED;
+  if ((int64_t)keep * Bs > (int64_t)INT32_MAX / 4) return IDX_ERR_UNSUPPORTED;
+  if (out_blocks && !aligned(out_blocks, 4)) return IDX_ERR_ALIGN;
+  GroupBlockPlan pl = plan_group_block(p, G, Bs, keep, nullptr, out_blocks);
+  if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
+  pl = plan_group_block(p, G, Bs, keep, align_ws(ws), out_blocks);
+
+  ProxyArgs pa;
+  pa.q = p->q; pa.q_dtype = p->q_dtype; pa.w = p->w; pa.q_pos = p->q_pos;
+  pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.D = p->D; pa.G = G; pa.n_groups = pl.NG;
+  pa.pq = pl.pq; pa.pw = pl.pw; pa.ppos = pl.ppos;
+  if ((st = from_hip(timed("proxy", s, [&] { return launch_proxy(pa, s); })))) return st;
+  PoolArgs po;
+  po.keys = p->k; po.k_dtype = p->k_dtype; po.k_len = p->k_len;
+  po.B = p->B; po.N = p->N; po.D = p->D; po.block_size = Bs; po.n_blocks = pl.NB;
+  po.pooled = pl.pooled;
+  if ((st = from_hip(timed("pool", s, [&] { return launch_pool(po, s); })))) return st;
+  // coarse: the proxies against the pooled blocks, block j sits at position j * Bs
+  for (int c0 = 0; c0 < pl.NG; c0 += pl.chunkP) {
+    const int c1 = std::min(pl.NG, c0 + pl.chunkP);
+    ScoreArgs a = base_score_args(p);
+    a.q = pl.pq; a.w = pl.pw; a.q_pos = pl.ppos; a.T = pl.NG;
+    a.keys = pl.pooled; a.k_scale = nullptr; a.key_cap = pl.NB;
+    a.pos_stride = Bs; a.count_div = Bs;
+    a.c0 = c0; a.c1 = c1;
+    a.scores = pl.cscores; a.score_stride = rstride(pl.NB); a.row_len = pl.row_len;
+    a.rows_per_seq = c1 - c0;
+    bool fused;
+    if ((st = from_hip(run_score(a, pl.NB, keep, pl.meta, &fused, s)))) return st;
+    TopkArgs t = topk_args(pl.cscores, rstride(pl.NB), pl.row_len, p->B * (c1 - c0), keep, c1 - c0, pl.NG,
+                           c0, pl.blocks, nullptr, keep);
+    t.out_count = pl.n_kept;
+    t.row_meta = fused ? pl.meta : nullptr;
+    t.digit_bits = a.digit_bits;
+    if ((st = from_hip(run_topk(t, pl.NB, s)))) return st;
+  }
+  if ((st = from_hip(timed("sort", s, [&] {
+         return launch_sort_rows(pl.blocks, keep, pl.n_kept, p->B * pl.NG, keep, pl.NB, s);
+       }))))
+    return st;
+  const int C = keep * Bs;
+  if ((st = from_hip(timed("sort", s, [&] {
+         return launch_expand_blocks(pl.blocks, pl.n_kept, keep, Bs, p->N, p->k_len, pl.NG, pl.list, pl.cnt,
+                                     p->B * pl.NG, s);
+       }))))
+    return st;
+  return refine_lists(p, k, G, C, pl.NG, pl.chunkG, pl.list, pl.cnt, pl.mscores, pl.row_len, pl.meta,
+                      out_idx, out_score, s);
+}
+
 RefinePlan plan_refine(const idx_problem* p, int G, int C, void* ws) {
   RefinePlan g;
   Carver c(ws);
@@ -662,6 +766,29 @@ int idx_group_proxy_reuse(const idx_problem* p, int32_t k, int32_t group_size, i
   } catch (...) {
     return IDX_ERR_INTERNAL;
   }
+}
+
+int idx_group_block_refine(const idx_problem* p, int32_t k, int32_t group_size, int32_t block_size,
+                           int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
+                           int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    return group_block_impl(p, k, group_size, block_size, n_blocks_keep, out_idx, out_score, out_blocks, ws,
+                            ws_bytes, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return IDX_ERR_INTERNAL;
+  }
+}
+
+size_t idx_group_block_workspace_bytes(const idx_problem* p, int32_t k, int32_t group_size,
+                                       int32_t block_size, int32_t n_blocks_keep) {
+  try {
+    if (!p || p->B <= 0 || p->T <= 0 || p->H <= 0 || p->D <= 0 || p->N <= 0 || k <= 0) return 0;
+    if (group_size < 1 || block_size < 1 || n_blocks_keep < 1) return 0;
+    if ((int64_t)n_blocks_keep * block_size > (int64_t)INT32_MAX / 4) return 0;
+    return plan_group_block(p, group_size, block_size, n_blocks_keep, nullptr, nullptr).bytes;
+  } catch (...) {
+  }
+  return 0;
 }
 
 int idx_refine_given(const idx_problem* p, int32_t k, int32_t group_size, const int32_t* cand,

@@ -122,6 +122,10 @@ hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_reuse_rows(const ReuseArgs& a, hipStream_t s);
+// kept blocks (ascending) -> ascending token lists inside the cache, keep * block_size per row
+hipError_t launch_expand_blocks(const int32_t* blocks, const int32_t* n_kept, int keep, int block_size,
+                                int N, const int32_t* k_len, int n_groups, int32_t* list, int32_t* cnt,
+                                int n_rows, hipStream_t s);
 // caller-supplied candidate lists -> ascending sets of ids in [0, k_len[b]) (rows of C entries)
 hipError_t launch_given_lists(const int32_t* src, const int32_t* cnt, int C, int N, const int32_t* k_len,
                               int n_groups, int32_t* dst, int32_t* dst_cnt, int n_rows, hipStream_t s);

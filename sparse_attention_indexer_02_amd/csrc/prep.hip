@@ -21,6 +21,9 @@
 // reuse_rows_kernel: PIVOT-Reuse ("PIVOT ...", abstract: the proxy's top-k is shared across the
 //   group). Reading: each member keeps the proxy's top-k tokens inside its own causal prefix,
 //   with the proxy's scores.
+//
+// expand_blocks_kernel: the block-filtered proxy (a PIVOT group proxy scoring HISA's pooled
+//   blocks): the kept blocks of a group become its candidate token list.
 #include "common.h"
 #include "kernels.h"
 
@@ -259,6 +262,37 @@ hipError_t launch_reuse_rows(const ReuseArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.T;
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(reuse_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Row r = b * n_groups + g: the first n_kept[r] block ids of blocks row r (ascending, `keep` per
+// row) become the ascending list of their tokens inside the cache, [0, k_len[b]), in row r of
+// `list` (keep * block_size entries), with the count in cnt[r]. Only the highest block can be
+// partial, so the tokens of block j start at entry j * block_size.
+__global__ void __launch_bounds__(256) expand_blocks_kernel(const int32_t* blocks, const int32_t* n_kept,
+                                                            int keep, int block_size, int N,
+                                                            const int32_t* k_len, int n_groups,
+                                                            int32_t* list, int32_t* cnt) {
+  const int r = blockIdx.x;
+  const int kl = k_len ? max(0, min(k_len[r / n_groups], N)) : N;
+  const int nk = min(max(n_kept[r], 0), keep);
+  const int32_t* brow = blocks + (int64_t)r * keep;
+  int32_t* out = list + (int64_t)r * keep * block_size;
+  const int total = nk * block_size;
+  for (int i = threadIdx.x; i < total; i += 256) {
+    const int tok = brow[i / block_size] * block_size + i % block_size;
+    out[i] = tok < kl ? tok : -1;
+  }
+  if (threadIdx.x == 0)
+    cnt[r] = nk > 0 ? (nk - 1) * block_size + min(block_size, kl - brow[nk - 1] * block_size) : 0;
+}
+
+hipError_t launch_expand_blocks(const int32_t* blocks, const int32_t* n_kept, int keep, int block_size,
+                                int N, const int32_t* k_len, int n_groups, int32_t* list, int32_t* cnt,
+                                int n_rows, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(expand_blocks_kernel, dim3(n_rows), dim3(256), 0, s, blocks, n_kept, keep, block_size,
+                     N, k_len, n_groups, list, cnt);
   return hipGetLastError();
 }
 

@@ -133,6 +133,18 @@ def test_reuse_arguments(L):
     assert L.idx_workspace_bytes(idx.OP_REUSE, ctypes.byref(p), 8, 0, 0) == 0
 
 
+def test_group_block_arguments(L):
+    p = _problem()
+    gb = lambda G, Bs, keep, pp=p, ws_bytes=1 << 40: L.idx_group_block_refine(
+        ctypes.byref(pp), 8, G, Bs, keep, 0x50000, None, None, 0x60000, ws_bytes, None)
+    assert gb(0, 16, 4) == -1 and gb(4, 0, 4) == -1 and gb(4, 16, 0) == -1
+    assert gb(4, 16, 40000) == -2
+    assert gb(4, 16, 4, pp=_problem(k_dtype=idx.FP8_E4M3, k_scale=0x70000)) == -2
+    assert gb(4, 16, 4, ws_bytes=100) == -4
+    assert L.idx_group_block_workspace_bytes(ctypes.byref(p), 8, 4, 16, 4) > 0
+    assert L.idx_group_block_workspace_bytes(ctypes.byref(p), 8, 0, 16, 4) == 0
+
+
 def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 4, 2, 32, dtype=torch.bfloat16)

@@ -234,6 +234,8 @@ WORKLOADS = {
                      gen=lambda seed=0: make_prefill(65536, 64, 128, seed=seed, rho=0.95)),
     "given16k": dict(op="given", k=2048, group_size=16, n_cand=4096,
                      gen=lambda seed=0: make_prefill(16384, 64, 128, seed=seed, rho=0.9)),
+    "gblock128k": dict(op="gblock", k=2048, group_size=16, block_size=128, n_blocks_keep=128,
+                       gen=lambda seed=0: make_hier(131072, 4096, seed=seed)),
     "hier128k": dict(op="block", k=2048, block_size=128, n_blocks_keep=128,
                      gen=lambda seed=0: make_hier(131072, 4096, seed=seed)),
 }
