@@ -153,6 +153,23 @@ def test_dense16k_full_size_sampled_rows():
     assert (gi[0].max(-1) <= np.arange(16384)).all()
 
 
+@pytest.mark.timeout(1200)
+def test_dense64k_full_size_sampled_rows():
+    # rows of 64K keys: 11-bit first digits in the score kernel's summary and the separate
+    # stream selector, whose boundary bin no longer fits on chip for the longest rows
+    spec = W.WORKLOADS["dense64k"]
+    p = spec["gen"](0)
+    say("case dense64k full size (L=65536, H=64, D=128, k=2048)")
+    gi, gs = run_dense(p, spec["k"])
+    rng = np.random.default_rng(1)
+    ts = sorted(set([0, 2047, 2048, 32767, 65535] + list(rng.integers(0, 65536, 7))))
+    flips = check_rows(p, spec["k"], gi, gs, [(0, t) for t in ts], "dense64k")
+    say(f"dense64k: {len(ts)} rows checked, {flips} tie-band swaps")
+    cnt = (gi[0] >= 0).sum(-1)
+    assert np.array_equal(cnt, np.minimum(spec["k"], np.arange(65536) + 1))
+    assert (gi[0].max(-1) <= np.arange(65536)).all()
+
+
 @pytest.mark.timeout(900)
 def test_decode128k_full_size_sampled_rows():
     spec = W.WORKLOADS["decode128k"]
