@@ -129,6 +129,19 @@ def test_long_rows_wide_boundary_bin():
         assert set(gi[0, t].tolist()) == set(range(k)), f"long t{t}"
 
 
+def test_stream_selector_long_boundary_bin_and_ties():
+    # fp32 queries: the separate stream selector; rows of all-zero scores longer than its
+    # candidate buffer re-read the row for each digit and keep the lowest slots of the tie
+    p = W.make_prefill(5000, 8, 64, seed=33, q_dtype=W.F32)
+    p.w[0, 4000:4003] = 0.0
+    k = 300
+    say("case stream selector: L=5000 fp32 queries, k=300, three all-zero rows")
+    gi, gs = run_dense(p, k)
+    check_rows(p, k, gi, gs, [(0, t) for t in (299, 300, 2500, 4000, 4002, 4999)], "stream-long")
+    for t in range(4000, 4003):
+        assert set(gi[0, t].tolist()) == set(range(k)), f"stream-long t{t}"
+
+
 def test_deterministic():
     p = W.make_prefill(600, 64, 128, seed=12)
     say("case determinism")
