@@ -553,6 +553,23 @@ __global__ void __launch_bounds__(TS_THREADS) topk_stream_kernel(TopkArgs a) {
   __syncthreads();
 
   if (kk > 0 && !all) {
+    // re-reads of the row when bin b1 does not fit: 16-byte loads clamped into the row's
+    // allocation, four per thread in flight, f(key) for every slot below n
+    const int lastf = (int)a.score_stride - 4;
+    auto sweep = [&](auto f) {
+      constexpr int FU = 4;
+      for (int base = 0; base < n; base += TS_THREADS * 4 * FU) {
+        f32x4_t v[FU];
+#pragma unroll
+        for (int q = 0; q < FU; ++q)
+          v[q] = *reinterpret_cast<const f32x4_t*>(srow + min(base + (q * TS_THREADS + tid) * 4, lastf));
+#pragma unroll
+        for (int q = 0; q < FU; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (base + (q * TS_THREADS + tid) * 4 + e < n) f(f2key(v[q][e]));
+      }
+    };
     // exact k-th key T among the slots of bin b1, and how many slots equal to T are kept
     uint32_t need = kk - above;
     const uint32_t nc = min(cnt[1], (uint32_t)TS_CAND);     // == c1 when it fits
@@ -561,10 +578,9 @@ __global__ void __launch_bounds__(TS_THREADS) topk_stream_kernel(TopkArgs a) {
     if (fits) {
       for (uint32_t j = tid; j < nc; j += TS_THREADS) atomicAdd(&hist[(ckey[j] >> 10) & m2], 1u);
     } else {
-      for (int i = tid; i < n; i += TS_THREADS) {
-        const uint32_t x = f2key(srow[i]);
+      sweep([&](uint32_t x) {
         if ((x >> s1) == b1) atomicAdd(&hist[(x >> 10) & m2], 1u);
-      }
+      });
     }
     __syncthreads();
     if (wave == 0) {
@@ -586,10 +602,9 @@ __global__ void __launch_bounds__(TS_THREADS) topk_stream_kernel(TopkArgs a) {
       for (uint32_t j = tid; j < nc; j += TS_THREADS)
         if ((ckey[j] >> 10) == pre) atomicAdd(&hist[ckey[j] & 0x3FFu], 1u);
     } else {
-      for (int i = tid; i < n; i += TS_THREADS) {
-        const uint32_t x = f2key(srow[i]);
+      sweep([&](uint32_t x) {
         if ((x >> 10) == pre) atomicAdd(&hist[x & 0x3FFu], 1u);
-      }
+      });
     }
     __syncthreads();
     if (wave == 0) {
@@ -634,32 +649,55 @@ __global__ void __launch_bounds__(TS_THREADS) topk_stream_kernel(TopkArgs a) {
       }
     } else {
       // keys of bin b1 above T are kept; equal ones by ascending slot: wave w takes a
-      // contiguous slot range, counts its equal keys, then takes its share of need_eq
-      const int chunk = ((n + TS_WAVES - 1) / TS_WAVES + 63) & ~63;
+      // contiguous slot range (a multiple of 256 slots, 4 consecutive slots per lane and step),
+      // counts its equal keys, then takes its share of need_eq
+      const int chunk = ((n + TS_WAVES - 1) / TS_WAVES + 255) & ~255;
       const int s0 = min(n, wave * chunk), e0 = min(n, s0 + chunk);
+      auto keys4 = [&](int i0, uint32_t (&x)[4]) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(srow + min(i0 + 4 * lane, lastf));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = i0 + 4 * lane + e < e0 ? f2key(v[e]) : 0u;
+      };
       uint32_t ce = 0;
-      for (int i0 = s0; i0 < e0; i0 += 64) {
-        const int i = i0 + lane;
-        const uint32_t x = i < e0 ? f2key(srow[i]) : 0u;
-        ce += (uint32_t)__popcll(__ballot(x == T && i < e0));
+      for (int i0 = s0; i0 < e0; i0 += 256) {
+        uint32_t x[4];
+        keys4(i0, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ce += x[e] == T ? 1u : 0u;
       }
+      ce = wave_bcast(wave_scan_dpp(ce), 63);
       if (lane == 0) weq[wave] = ce;
       __syncthreads();
       uint32_t eb = 0;
       for (int w = 0; w < wave; ++w) eb += weq[w];
-      for (int i0 = s0; i0 < e0; i0 += 64) {
-        const int i = i0 + lane;
-        const uint32_t x = i < e0 ? f2key(srow[i]) : 0u;
-        const bool gt = (x >> s1) == b1 && x > T && i < e0;
-        const bool eq = x == T && i < e0;
-        const uint64_t me = __ballot(eq);
-        const bool sel = gt || (eq && eb + lanes_below(me) < need_eq);
-        const uint64_t m = __ballot(sel);
+      for (int i0 = s0; i0 < e0; i0 += 256) {
+        uint32_t x[4];
+        keys4(i0, x);
+        uint32_t eqc = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) eqc += x[e] == T ? 1u : 0u;
+        const uint32_t einc = wave_scan_dpp(eqc);
+        uint32_t rk = eb + einc - eqc;                   // rank of this lane's first equal slot
+        bool sel[4];
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool eq = x[e] == T;
+          sel[e] = ((x[e] >> s1) == b1 && x[e] > T) || (eq && rk < need_eq);
+          rk += eq ? 1u : 0u;
+          c += sel[e] ? 1u : 0u;
+        }
+        const uint32_t inc = wave_scan_dpp(c);
+        const uint32_t tot = wave_bcast(inc, 63);
         uint32_t pb = 0;
-        if (lane == 0 && m) pb = atomicAdd(&cnt[0], (uint32_t)__popcll(m));
-        pb = wave_bcast(pb, 0);
-        if (sel) emit(pb + lanes_below(m), i, x);
-        eb += (uint32_t)__popcll(me);
+        if (lane == 0 && tot) pb = atomicAdd(&cnt[0], tot);
+        pb = wave_bcast(pb, 0) + inc - c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (sel[e]) emit(pb, i0 + 4 * lane + e, x[e]);
+          pb += sel[e] ? 1u : 0u;
+        }
+        eb += wave_bcast(einc, 63);
       }
     }
   }
