@@ -1,12 +1,18 @@
 """Benchmark of the MI355X DSA lightning indexer.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense16k] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --copy-probe BYTES     (a plain device copy of known size, for calibrating
                                             the HBM byte counters of rocprofv3 --pmc)
 
 One step = one full indexer call (every stage of the path: scoring, masking, top-k selection,
 and for the variants the proxy / pooling / candidate stages) over one batch of seeded synthetic
 input that is already resident in HBM. Prints ONE JSON line.
+
+Without --workload the line is the metric's headline: the 64K prefill (dense64k) is the timed
+step and its numbers are the line's value; the 128K decode step (decode128k) is timed after it
+with the same steps and warmup and carried in the same line under "decode128k". With --workload
+NAME the line is that workload alone; the group and block variants also report recall@k of their
+selections against the dense indexer's GPU selection on the same inputs.
 
 value = query-key pairs per second: the causally visible (query, key) pairs of the workload
 (the work the dense indexer does; for the group and block variants this is the
@@ -41,7 +47,7 @@ def log(*a):
 
 # source files each profiled kernel is compiled from (its own file and the headers it includes)
 KERNEL_SOURCES = {
-    "score_kernel": ["score.hip", "score_tile.h", "common.h", "kernels.h"],
+    "score_kernel": ["score_kernel.h", "score_tile.h", "common.h", "kernels.h"],
     "decode_scan_kernel": ["decode.hip", "common.h", "kernels.h"],
     "block_refine_kernel": ["block_refine.hip", "score_tile.h", "common.h", "kernels.h"],
     "block_refine_direct_kernel": ["block_refine.hip", "score_tile.h", "common.h", "kernels.h"],
@@ -261,7 +267,232 @@ def cpu_oracle_baseline(name, spec, prob, budget_s=12.0):
         sample = f"{rows} query rows of {T} (interleaved with stride {stride}), pooling + coarse + refine"
     dt = time.perf_counter() - t0
     return {"value": done_pairs / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample + f"; {dt:.1f} s; dense-equivalent pairs"}
+            "sample": sample + f"; {dt:.1f} s; dense-equivalent pairs", **host_info(threads)}
+
+
+def host_info(blas_threads):
+    """The host the oracle ran on: logical CPUs of the machine and of this process, the BLAS
+    thread count the oracle's matrix products used (= `cores`), and the CPU model."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    return {"host_nproc": os.cpu_count() or 1, "host_cpus_available": avail,
+            "oracle_threads": int(blas_threads), "cpu_model": model}
+
+
+
+
+# ----------------------------------------------------------------------------------------------
+
+class Run:
+    """One workload on the GPU: inputs in HBM, outputs and workspace allocated once, `step()`
+    enqueues one full indexer call."""
+
+    def __init__(self, name, seed):
+        import torch
+        import workloads as W
+        import sparse_attention_indexer_02_amd as idx
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from gpu_util import dev
+        self.name, self.seed = name, seed
+        self.spec = spec = W.WORKLOADS[name]
+        log(f"[bench] generating {name} (seed {seed})")
+        self.prob = prob = spec["gen"](seed)
+        self.t = t = dev(prob, "cuda:0")
+        self.k = k = spec["k"]
+        B, T = prob.B, prob.T
+        self.op = op = spec["op"]
+        self.out_idx = torch.empty((B, T, k), dtype=torch.int32, device="cuda:0")
+        self.out_sc = torch.empty((B, T, k), dtype=torch.float32, device="cuda:0")
+        p = idx.make_problem(t["q"], t["k"], t["w"], t["q_pos"], t["k_len"], t["k_scale"])
+        self.banks_np = None
+        if op == "dense":
+            need = idx.workspace_bytes(idx.OP_SCORE_TOPK, p, k)
+        elif op == "group":
+            need = idx.workspace_bytes(idx.OP_GROUP, p, k, spec["group_size"], spec["n_cand"])
+        elif op == "reuse":
+            need = idx.workspace_bytes(idx.OP_REUSE, p, k, spec["group_size"], 0)
+        elif op == "gblock":
+            need = int(idx.lib().idx_group_block_workspace_bytes(ctypes.byref(p), k, spec["group_size"],
+                                                                  spec["block_size"], spec["n_blocks_keep"]))
+        elif op == "given":
+            self.banks_np = W.make_banks(prob, spec["group_size"], spec["n_cand"], seed)
+            self.banks = torch.from_numpy(self.banks_np).to("cuda:0")
+            need = idx.workspace_bytes(idx.OP_REFINE, p, k, spec["group_size"], spec["n_cand"])
+        else:
+            need = idx.workspace_bytes(idx.OP_BLOCK, p, k, spec["block_size"], spec["n_blocks_keep"])
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+
+    def step(self):
+        import sparse_attention_indexer_02_amd as idx
+        t, k, spec, op = self.t, self.k, self.spec, self.op
+        kw = dict(k_len=t["k_len"], out_idx=self.out_idx, out_score=self.out_sc, workspace=self.ws)
+        if op == "dense":
+            idx.score_topk(t["q"], t["k"], t["w"], t["q_pos"], topk=k, k_scale=t["k_scale"], **kw)
+        elif op == "group":
+            idx.group_proxy_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
+                                   group_size=spec["group_size"], n_cand=spec["n_cand"],
+                                   k_scale=t["k_scale"], **kw)
+        elif op == "gblock":
+            idx.group_block_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
+                                   group_size=spec["group_size"], block_size=spec["block_size"],
+                                   n_blocks_keep=spec["n_blocks_keep"], **kw)
+        elif op == "reuse":
+            idx.group_proxy_reuse(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
+                                  group_size=spec["group_size"], k_scale=t["k_scale"], **kw)
+        elif op == "given":
+            idx.refine_given(t["q"], t["k"], t["w"], t["q_pos"], self.banks, topk=k,
+                             group_size=spec["group_size"], k_scale=t["k_scale"], **kw)
+        else:
+            idx.block_coarse_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
+                                    block_size=spec["block_size"],
+                                    n_blocks_keep=spec["n_blocks_keep"], **kw)
+
+    def time(self, steps, warmup):
+        """Mean step time (HIP events around exactly `steps` steps after `warmup` untimed ones)
+        and the library's per-kernel event totals over the timed steps."""
+        import torch
+        import sparse_attention_indexer_02_amd as idx
+        log(f"[bench] {self.name}: warmup {warmup}")
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        idx.timer_enable(True)
+        log(f"[bench] {self.name}: timing {steps} steps")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        torch.cuda.synchronize()
+        self.wall = time.perf_counter() - w0
+        self.ms_step = e0.elapsed_time(e1) / steps
+        self.steps = steps
+        self.kernels = {n: idx.timer_read(n)
+                        for n in ("score", "topk", "sort", "proxy", "pool", "block_refine", "reuse",
+                                  "decode_scan", "decode_select")}
+        idx.timer_enable(False)
+        log(f"[bench] {self.name}: {self.ms_step:.4f} ms/step; per-kernel ms/step: " + ", ".join(
+            f"{n} {ms / steps:.3f} ({c // max(1, steps)} launches)"
+            for n, (ms, c) in self.kernels.items() if c))
+
+    def _mfma(self, kernel, flops, **extra):
+        ms, n = self.kernels["block_refine" if kernel.startswith("block_refine") else "score"]
+        per_launch = flops / (n / self.steps)
+        achieved = per_launch / (ms / n * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(self.name, kernel),
+                "per_launch": f"{per_launch:.4g} flop", "mean_launch_ms": ms / n, **extra}
+
+    def report(self):
+        """(config, roofline) of the timed run."""
+        import workloads as W
+        prob, spec, op = self.prob, self.spec, self.op
+        cfg = {"workload": self.name, "B": prob.B, "T": prob.T, "H": prob.H, "D": prob.D,
+               "N": prob.N, "k": self.k, "q_dtype": W.DTYPE_NAMES[prob.q_dtype],
+               "k_dtype": W.DTYPE_NAMES[prob.k_dtype], "seed": self.seed,
+               "pairs_per_step": prob.pairs()}
+        if op == "dense" and self.kernels["decode_scan"][1] == 0:
+            roof = self._mfma("score_kernel", dense_flops(prob))
+        elif op == "dense":
+            # decode shape: the streaming scan is the dominant kernel, bound by the key-cache read
+            ms, n = self.kernels["decode_scan"]
+            byts = decode_bytes(prob)
+            per_launch = byts / (n / self.steps)
+            achieved = per_launch / (ms / n * 1e-3) / 1e9
+            roof = {"bound": "hbm", "kernel": "decode_scan_kernel", "achieved": achieved,
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                    "traffic": measured_traffic(self.name, "decode_scan_kernel"),
+                    "per_launch": f"{per_launch:.4g} B", "mean_launch_ms": ms / n}
+        elif op == "group":
+            pp, rp = group_refine_pairs(prob, spec["group_size"], spec["n_cand"])
+            roof = self._mfma("score_kernel", 2.0 * prob.H * prob.D * (pp + rp))
+            cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"],
+                       algorithmic_pairs_per_step=pp + rp)
+        elif op == "gblock":
+            G, Bs, keep = spec["group_size"], spec["block_size"], spec["n_blocks_keep"]
+            rp = gblock_refine_pairs(prob, G, Bs, keep)
+            roof = self._mfma("score_kernel", 2.0 * prob.H * prob.D * rp,
+                              note="score kernel time covers the proxies' block scan and the member "
+                                   "refine; the flops are the refine's")
+            cfg.update(group_size=G, block_size=Bs, n_blocks_keep=keep, algorithmic_pairs_per_step=rp)
+        elif op == "reuse":
+            pp, _ = group_refine_pairs(prob, spec["group_size"], 1)
+            roof = self._mfma("score_kernel", 2.0 * prob.H * prob.D * pp)
+            cfg.update(group_size=spec["group_size"], algorithmic_pairs_per_step=pp)
+        elif op == "given":
+            rp = given_pairs(prob, spec["group_size"], self.banks_np)
+            roof = self._mfma("score_kernel", 2.0 * prob.H * prob.D * rp)
+            cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"], algorithmic_pairs_per_step=rp)
+        else:
+            cp, rp = block_pairs(prob, spec["block_size"], spec["n_blocks_keep"])
+            roof = self._mfma(block_refine_kernel_name(prob, spec["block_size"]),
+                              2.0 * prob.H * prob.D * rp)
+            cfg.update(block_size=spec["block_size"], n_blocks_keep=spec["n_blocks_keep"],
+                       algorithmic_pairs_per_step=cp + rp)
+        cfg["kernel_ms_per_step"] = {n_: round(ms_ / self.steps, 4)
+                                     for n_, (ms_, c) in self.kernels.items() if c}
+        return cfg, roof
+
+    def recall_vs_dense(self):
+        """recall@k of the last step's selections against the dense indexer's GPU selection on
+        the same inputs: |S_variant & S_dense| / |S_dense| summed over every query row. The dense
+        path is the one the parity tests check against the oracle."""
+        import torch
+        import sparse_attention_indexer_02_amd as idx
+        t = self.t
+        d_idx, _ = idx.score_topk(t["q"], t["k"], t["w"], t["q_pos"], topk=self.k, k_len=t["k_len"],
+                                  k_scale=t["k_scale"], want_score=False)
+        v = self.out_idx.reshape(-1, self.k)
+        d = d_idx.reshape(-1, self.k)
+        hit = tot = 0
+        for r0 in range(0, v.shape[0], 2048):
+            vs = torch.sort(v[r0:r0 + 2048], dim=-1).values.contiguous()
+            ds = torch.sort(d[r0:r0 + 2048], dim=-1).values.contiguous()
+            pos = torch.searchsorted(vs, ds).clamp_(max=self.k - 1)
+            found = (torch.gather(vs, 1, pos) == ds) & (ds >= 0)
+            hit += int(found.sum())
+            tot += int((ds >= 0).sum())
+        torch.cuda.synchronize()
+        return {"recall_at_k": hit / max(1, tot), "rows": int(v.shape[0]), "dense_selected": tot,
+                "reference": "dense indexer (idx_score_topk) on the same inputs, GPU"}
+
+    def line(self, cpu=True):
+        """The workload's numbers: ms/step, pairs/s, rows/s, roofline, oracle baseline."""
+        cfg, roof = self.report()
+        prob = self.prob
+        out = {"ms_per_step": self.ms_step, "value": prob.pairs() / (self.ms_step * 1e-3),
+               "unit": "pairs/s", "topk_rows_per_s": prob.B * prob.T / (self.ms_step * 1e-3),
+               "config": cfg, "roofline": roof, "wall_s_timed": self.wall}
+        if self.op != "dense":
+            log(f"[bench] {self.name}: recall vs the dense indexer")
+            out["recall_vs_dense"] = self.recall_vs_dense()
+        out["cpu_baseline"] = None
+        if cpu:
+            log(f"[bench] {self.name}: timing the CPU oracle on a row sample")
+            out["cpu_baseline"] = cpu_oracle_baseline(self.name, self.spec, prob)
+        return out
+
+    def free(self):
+        import torch
+        for a in ("t", "out_idx", "out_sc", "ws", "banks"):
+            if hasattr(self, a):
+                delattr(self, a)
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -269,7 +500,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense16k")
+    ap.add_argument("--workload", default=None,
+                    help="one workload alone (default: the headline, dense64k with decode128k)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
@@ -282,187 +514,28 @@ def main():
         copy_probe(args.copy_probe)
         return
 
-    import numpy as np
-    import torch
+    headline = args.workload is None
+    name = "dense64k" if headline else args.workload
+    run = Run(name, args.seed)
+    run.time(args.steps, args.warmup)
+    main_line = run.line(cpu=not args.no_cpu)
+    q_dtype = run.prob.q_dtype
+    run.free()
     import workloads as W
-    import sparse_attention_indexer_02_amd as idx
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import dev
-
-    spec = W.WORKLOADS[args.workload]
-    log(f"[bench] generating {args.workload} (seed {args.seed})")
-    prob = spec["gen"](args.seed)
-    t = dev(prob, "cuda:0")
-    k = spec["k"]
-    B, T = prob.B, prob.T
-    op = spec["op"]
-    out_idx = torch.empty((B, T, k), dtype=torch.int32, device="cuda:0")
-    out_sc = torch.empty((B, T, k), dtype=torch.float32, device="cuda:0")
-    p = idx.make_problem(t["q"], t["k"], t["w"], t["q_pos"], t["k_len"], t["k_scale"])
-    if op == "dense":
-        need = idx.workspace_bytes(idx.OP_SCORE_TOPK, p, k)
-    elif op == "group":
-        need = idx.workspace_bytes(idx.OP_GROUP, p, k, spec["group_size"], spec["n_cand"])
-    elif op == "reuse":
-        need = idx.workspace_bytes(idx.OP_REUSE, p, k, spec["group_size"], 0)
-    elif op == "gblock":
-        need = int(idx.lib().idx_group_block_workspace_bytes(ctypes.byref(p), k, spec["group_size"],
-                                                              spec["block_size"], spec["n_blocks_keep"]))
-    elif op == "given":
-        banks_np = W.make_banks(prob, spec["group_size"], spec["n_cand"], args.seed)
-        banks = torch.from_numpy(banks_np).to("cuda:0")
-        need = idx.workspace_bytes(idx.OP_REFINE, p, k, spec["group_size"], spec["n_cand"])
-    else:
-        need = idx.workspace_bytes(idx.OP_BLOCK, p, k, spec["block_size"], spec["n_blocks_keep"])
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
-
-    def step():
-        if op == "dense":
-            idx.score_topk(t["q"], t["k"], t["w"], t["q_pos"], topk=k, k_len=t["k_len"],
-                           k_scale=t["k_scale"], out_idx=out_idx, out_score=out_sc, workspace=ws)
-        elif op == "group":
-            idx.group_proxy_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
-                                   group_size=spec["group_size"], n_cand=spec["n_cand"],
-                                   k_len=t["k_len"], k_scale=t["k_scale"], out_idx=out_idx,
-                                   out_score=out_sc, workspace=ws)
-        elif op == "gblock":
-            idx.group_block_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
-                                   group_size=spec["group_size"], block_size=spec["block_size"],
-                                   n_blocks_keep=spec["n_blocks_keep"], k_len=t["k_len"],
-                                   out_idx=out_idx, out_score=out_sc, workspace=ws)
-        elif op == "reuse":
-            idx.group_proxy_reuse(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
-                                  group_size=spec["group_size"], k_len=t["k_len"],
-                                  k_scale=t["k_scale"], out_idx=out_idx, out_score=out_sc,
-                                  workspace=ws)
-        elif op == "given":
-            idx.refine_given(t["q"], t["k"], t["w"], t["q_pos"], banks, topk=k,
-                             group_size=spec["group_size"], k_len=t["k_len"], k_scale=t["k_scale"],
-                             out_idx=out_idx, out_score=out_sc, workspace=ws)
-        else:
-            idx.block_coarse_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
-                                    block_size=spec["block_size"],
-                                    n_blocks_keep=spec["n_blocks_keep"], k_len=t["k_len"],
-                                    out_idx=out_idx, out_score=out_sc, workspace=ws)
-
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    idx.timer_enable(True)
-    log(f"[bench] timing {args.steps} steps")
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    kernels = {name: idx.timer_read(name)
-               for name in ("score", "topk", "sort", "proxy", "pool", "block_refine", "reuse",
-                            "decode_scan", "decode_select")}
-    idx.timer_enable(False)
-    log("[bench] per-kernel ms/step: " + ", ".join(
-        f"{n} {ms / args.steps:.3f} ({c // max(1, args.steps)} launches)" for n, (ms, c) in kernels.items() if c))
-
-    pairs = prob.pairs()
-    value = pairs / (ms_step * 1e-3)
-    rows_per_s = B * T / (ms_step * 1e-3)
-    cfg = {"workload": args.workload, "B": B, "T": T, "H": prob.H, "D": prob.D, "N": prob.N,
-           "k": k, "q_dtype": W.DTYPE_NAMES[prob.q_dtype], "k_dtype": W.DTYPE_NAMES[prob.k_dtype],
-           "seed": args.seed, "pairs_per_step": pairs}
-    if op == "dense" and kernels["decode_scan"][1] == 0:
-        dom = "score"
-        ms, n = kernels["score"]
-        flops = dense_flops(prob)
-        achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(args.workload, "score_kernel"),
-                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
-    elif op == "dense":
-        # decode shape: the streaming scan is the dominant kernel, bound by the key-cache read
-        ms, n = kernels["decode_scan"]
-        byts = decode_bytes(prob)
-        achieved = byts / (n / args.steps) / (ms / n * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "decode_scan_kernel", "achieved": achieved,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "traffic": measured_traffic(args.workload, "decode_scan_kernel"),
-                "per_launch": f"{byts / (n / args.steps):.4g} B",
-                "mean_launch_ms": ms / n}
-    elif op == "group":
-        pp, rp = group_refine_pairs(prob, spec["group_size"], spec["n_cand"])
-        ms, n = kernels["score"]
-        flops = 2.0 * prob.H * prob.D * (pp + rp)
-        achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(args.workload, "score_kernel"),
-                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
-        cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"],
-                   algorithmic_pairs_per_step=pp + rp)
-    elif op == "gblock":
-        G, Bs, keep = spec["group_size"], spec["block_size"], spec["n_blocks_keep"]
-        rp = gblock_refine_pairs(prob, G, Bs, keep)
-        ms, n = kernels["score"]
-        flops = 2.0 * prob.H * prob.D * rp
-        achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(args.workload, "score_kernel"),
-                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n,
-                "note": "score kernel time covers the proxies' block scan and the member refine; "
-                        "the flops are the refine's"}
-        cfg.update(group_size=G, block_size=Bs, n_blocks_keep=keep, algorithmic_pairs_per_step=rp)
-    elif op == "reuse":
-        pp, _ = group_refine_pairs(prob, spec["group_size"], 1)
-        ms, n = kernels["score"]
-        flops = 2.0 * prob.H * prob.D * pp
-        achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(args.workload, "score_kernel"),
-                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
-        cfg.update(group_size=spec["group_size"], algorithmic_pairs_per_step=pp)
-    elif op == "given":
-        rp = given_pairs(prob, spec["group_size"], banks_np)
-        ms, n = kernels["score"]
-        flops = 2.0 * prob.H * prob.D * rp
-        achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "score_kernel", "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(args.workload, "score_kernel"),
-                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
-        cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"], algorithmic_pairs_per_step=rp)
-    else:
-        cp, rp = block_pairs(prob, spec["block_size"], spec["n_blocks_keep"])
-        ms, n = kernels["block_refine"]
-        flops = 2.0 * prob.H * prob.D * rp
-        achieved = flops / (n / args.steps) / (ms / n * 1e-3) / 1e12
-        kname = block_refine_kernel_name(prob, spec["block_size"])
-        roof = {"bound": "mfma", "kernel": kname, "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(args.workload, kname),
-                "per_launch": f"{flops / (n / args.steps):.4g} flop", "mean_launch_ms": ms / n}
-        cfg.update(block_size=spec["block_size"], n_blocks_keep=spec["n_blocks_keep"],
-                   algorithmic_pairs_per_step=cp + rp)
-    cfg["kernel_ms_per_step"] = {n_: round(ms_ / args.steps, 4) for n_, (ms_, c) in kernels.items() if c}
-
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] timing the CPU oracle on a row sample")
-        cpu = cpu_oracle_baseline(args.workload, spec, prob)
-
-    out = {"metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if prob.q_dtype == W.BF16 else "f32",
-           "data": "synthetic (seeded generators shaped like the pages' workloads)",
-           "config": cfg, "topk_rows_per_s": rows_per_s, "roofline": roof, "cpu_baseline": cpu,
-           "wall_s_timed": wall}
+    out = {"metric": METRIC, "value": main_line["value"], "unit": "pairs/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_line["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if q_dtype == W.BF16 else "f32",
+           "data": "synthetic (seeded generators shaped like the pages' workloads)"}
+    out.update({k_: v_ for k_, v_ in main_line.items() if k_ not in out})
+    if headline:
+        dec = Run("decode128k", args.seed)
+        dec.time(args.steps, args.warmup)
+        d = dec.line(cpu=not args.no_cpu)
+        d["dtype"] = "bf16 queries x fp8 e4m3 keys (bf16 MFMA, fp32 accumulate)"
+        d["steps"], d["warmup"] = args.steps, args.warmup
+        out["decode128k"] = d
+        dec.free()
     print(json.dumps(out))
 
 

@@ -101,7 +101,8 @@ int idx_score_topk(const idx_problem* p, int32_t k, int32_t* out_idx, float* out
  *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
  *   out_cand [B, ceil(T/group_size), n_cand] int32 (optional): each group's candidates in
  *            ascending token order, -1 padded.
- * With n_cand >= the prefix length the result equals idx_score_topk's. Requires n_cand <= N.
+ * A proxy keeps min(n_cand, its prefix length) candidates, so any n_cand >= 1 is valid; with
+ * n_cand >= the prefix length the result equals idx_score_topk's.
  * In decode, a group is the queries decoded together in one multi-token-prediction step (same
  * abstract): pass group_size = T, the number of MTP queries per sequence. */
 int idx_group_proxy_refine(const idx_problem* p, int32_t k, int32_t group_size, int32_t n_cand,
@@ -193,8 +194,10 @@ const char* idx_strerror(int status);
  * the kernels whose name contains `kernel_substr` (all kernels if NULL or ""); kernel names are
  * "score", "topk", "sort", "proxy", "pool", "block_refine", "reuse", "decode_scan" and
  * "decode_select".
- * idx_timer_enable(on) clears the record
- * and switches recording on or off. Not thread safe. */
+ * idx_timer_enable(on) clears the record and switches recording on or off; switching it on
+ * creates a pool of 8192 HIP events once (IDX_ERR_HIP if that fails), so library calls never
+ * create events. At most 4096 launches are recorded per enable; idx_timer_read returns
+ * IDX_ERR_INTERNAL (with the recorded totals) when launches went unrecorded. Not thread safe. */
 int idx_timer_enable(int on);
 int idx_timer_read(const char* kernel_substr, double* total_ms, int32_t* launches);
 

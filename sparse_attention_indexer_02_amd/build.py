@@ -18,7 +18,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libidx.so")
-SOURCES = ["abi.hip", "score.hip", "block_refine.hip", "decode.hip", "topk.hip", "prep.hip"]
+SOURCES = ["abi.hip", "score.hip", "score_bb128.hip", "score_bb64.hip", "score_bb32_b8.hip",
+           "score_f32_f32_d128.hip", "score_f32_bf16_d128.hip", "score_f32_fp8_d128.hip",
+           "score_f32_f32_d32_64.hip", "score_f32_bf16_d32_64.hip", "score_f32_fp8_d32_64.hip",
+           "block_refine.hip", "decode.hip", "topk.hip", "prep.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -46,7 +49,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(os.cpu_count() or 8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]

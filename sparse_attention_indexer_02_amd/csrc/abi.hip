@@ -34,25 +34,30 @@ bool g_timer_on = false;
 std::vector<TimerRec> g_recs;
 std::vector<hipEvent_t> g_event_pool;
 
+// Events are created by idx_timer_enable only (library calls never create them); a launch that
+// finds the pool empty is not recorded and counted in g_dropped.
+constexpr size_t kTimerEvents = 8192;
+int g_dropped = 0;
+
 hipEvent_t pool_event() {
-  if (!g_event_pool.empty()) {
-    hipEvent_t e = g_event_pool.back();
-    g_event_pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (g_event_pool.empty()) return nullptr;
+  hipEvent_t e = g_event_pool.back();
+  g_event_pool.pop_back();
   return e;
 }
 
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& f) {
   if (!g_timer_on) return f();
+  if (g_event_pool.size() < 2) {
+    ++g_dropped;
+    return f();
+  }
   hipEvent_t a = pool_event(), b = pool_event();
-  if (a) hipEventRecord(a, s);
+  hipEventRecord(a, s);
   hipError_t e = f();
-  if (b) hipEventRecord(b, s);
-  if (a && b) g_recs.push_back({name, a, b});
+  hipEventRecord(b, s);
+  g_recs.push_back({name, a, b});
   return e;
 }
 
@@ -174,7 +179,7 @@ struct RefinePlan {
 };
 
 struct GroupPlan {
-  int NG, chunkP, chunkG;
+  int NG, chunkP, chunkG, Cs;
   void* pq;
   float* pw;
   int32_t* ppos;
@@ -187,20 +192,24 @@ struct GroupPlan {
   size_t bytes;
 };
 
+// C is the caller's candidate count; a proxy keeps at most its prefix, so buffers are sized for
+// min(C, N) candidates (Ce), and candidate rows have the caller's stride C only in out_cand.
 GroupPlan plan_group(const idx_problem* p, int G, int C, void* ws, int32_t* out_cand) {
   GroupPlan g;
   Carver c(ws);
   g.NG = (p->T + G - 1) / G;
+  const int Ce = std::min(C, p->N);
+  g.Cs = out_cand ? C : Ce;
   const size_t qeb = p->q_dtype == IDX_BF16 ? 2 : 4;
   g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
   g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
   g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
   g.chunkP = chunk_rows(p->B, rstride(p->N) * 4, g.NG);
   g.pscores = c.take<float>((size_t)p->B * g.chunkP * rstride(p->N));
-  g.cand = out_cand ? out_cand : c.take<int32_t>((size_t)p->B * g.NG * C);
+  g.cand = out_cand ? out_cand : c.take<int32_t>((size_t)p->B * g.NG * Ce);
   g.cand_cnt = c.take<int32_t>((size_t)p->B * g.NG);
-  g.chunkG = chunk_rows(p->B, (int64_t)G * rstride(C) * 4, g.NG);
-  g.mscores = c.take<float>((size_t)p->B * std::min(p->T, g.chunkG * G) * rstride(C));
+  g.chunkG = chunk_rows(p->B, (int64_t)G * rstride(Ce) * 4, g.NG);
+  g.mscores = c.take<float>((size_t)p->B * std::min(p->T, g.chunkG * G) * rstride(Ce));
   g.row_len = c.take<int32_t>((size_t)p->B * std::max(std::min(p->T, g.chunkG * G), g.chunkP));
   g.meta = c.take<int32_t>((size_t)p->B * std::max(std::min(p->T, g.chunkG * G), g.chunkP) * 4);
   g.bytes = c.off + kAlign;
@@ -403,16 +412,17 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
 // Per-query refine over per-group candidate lists (rows of C token ids in ascending order, the
 // first cnt[b * NG + g] used): members t of group g score the list's tokens inside their own
 // prefix (LIST mode of the score kernel) and keep their top k, mapped back to tokens.
-int refine_lists(const idx_problem* p, int32_t k, int G, int C, int NG, int chunkG, const int32_t* list,
-                 const int32_t* cnt, float* mscores, int32_t* row_len, int32_t* meta, int32_t* out_idx,
-                 float* out_score, hipStream_t s) {
+// Lists have stride Ls (entries per row) and hold at most C ids.
+int refine_lists(const idx_problem* p, int32_t k, int G, int C, int Ls, int NG, int chunkG,
+                 const int32_t* list, const int32_t* cnt, float* mscores, int32_t* row_len, int32_t* meta,
+                 int32_t* out_idx, float* out_score, hipStream_t s) {
   int st;
   for (int g0 = 0; g0 < NG; g0 += chunkG) {
     const int g1 = std::min(NG, g0 + chunkG);
     const int rows = std::min(p->T, g1 * G) - g0 * G;
     ScoreArgs a = base_score_args(p);
     a.mode = MODE_LIST;
-    a.list = list; a.list_len = cnt; a.list_stride = C; a.group_size = G;
+    a.list = list; a.list_len = cnt; a.list_stride = Ls; a.group_size = G;
     a.n_groups = NG;
     a.c0 = g0; a.c1 = g1;
     a.scores = mscores; a.score_stride = rstride(C); a.row_len = row_len;
@@ -424,7 +434,7 @@ int refine_lists(const idx_problem* p, int32_t k, int G, int C, int NG, int chun
     t.row_meta = fused ? meta : nullptr;
     t.digit_bits = a.digit_bits;
     t.map_mode = MAP_LIST;
-    t.list = list; t.list_stride = C; t.group_size = G; t.n_groups = NG;
+    t.list = list; t.list_stride = Ls; t.group_size = G; t.n_groups = NG;
     if ((st = from_hip(run_topk(t, C, s)))) return st;
   }
   return IDX_OK;
@@ -434,11 +444,13 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
                float* out_score, int32_t* out_cand, void* ws, size_t ws_bytes, hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
-  if (G < 1 || C < 1 || C > p->N) return IDX_ERR_INVALID_ARG;
+  if (G < 1 || C < 1) return IDX_ERR_INVALID_ARG;
   if (out_cand && !aligned(out_cand, 4)) return IDX_ERR_ALIGN;
   GroupPlan pl = plan_group(p, G, C, nullptr, out_cand);
   if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
   pl = plan_group(p, G, C, align_ws(ws), out_cand);
+  // a proxy keeps min(C, its prefix) candidates; the selection pads candidate rows to Cs entries
+  const int Ce = std::min(C, p->N), Cs = pl.Cs;
 
   ProxyArgs pa;
   pa.q = p->q; pa.q_dtype = p->q_dtype; pa.w = p->w; pa.q_pos = p->q_pos;
@@ -455,9 +467,9 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
     a.scores = pl.pscores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
     bool fused;
-    if ((st = from_hip(run_score(a, p->N, C, pl.meta, &fused, s)))) return st;
-    TopkArgs t = topk_args(pl.pscores, rstride(p->N), pl.row_len, p->B * (c1 - c0), C, c1 - c0, pl.NG, c0,
-                           pl.cand, nullptr, C);
+    if ((st = from_hip(run_score(a, p->N, Cs, pl.meta, &fused, s)))) return st;
+    TopkArgs t = topk_args(pl.pscores, rstride(p->N), pl.row_len, p->B * (c1 - c0), Cs, c1 - c0, pl.NG, c0,
+                           pl.cand, nullptr, Cs);
     t.out_count = pl.cand_cnt;
     t.row_meta = fused ? pl.meta : nullptr;
     t.digit_bits = a.digit_bits;
@@ -465,10 +477,10 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
   }
   // candidate lists in ascending token order (the refine indexes them by slot)
   if ((st = from_hip(timed("sort", s, [&] {
-         return launch_sort_rows(pl.cand, C, pl.cand_cnt, p->B * pl.NG, C, p->N, s);
+         return launch_sort_rows(pl.cand, Cs, pl.cand_cnt, p->B * pl.NG, Ce, p->N, s);
        }))))
     return st;
-  return refine_lists(p, k, G, C, pl.NG, pl.chunkG, pl.cand, pl.cand_cnt, pl.mscores, pl.row_len,
+  return refine_lists(p, k, G, Ce, Cs, pl.NG, pl.chunkG, pl.cand, pl.cand_cnt, pl.mscores, pl.row_len,
                       pl.meta, out_idx, out_score, s);
 }
 
@@ -614,7 +626,7 @@ int group_block_impl(const idx_problem* p, int32_t k, int32_t G, int32_t Bs, int
                                      p->B * pl.NG, s);
        }))))
     return st;
-  return refine_lists(p, k, G, C, pl.NG, pl.chunkG, pl.list, pl.cnt, pl.mscores, pl.row_len, pl.meta,
+  return refine_lists(p, k, G, C, C, pl.NG, pl.chunkG, pl.list, pl.cnt, pl.mscores, pl.row_len, pl.meta,
                       out_idx, out_score, s);
 }
 
@@ -649,7 +661,7 @@ int refine_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, const int
          return launch_given_lists(cand, cand_cnt, C, p->N, p->k_len, pl.NG, pl.list, pl.cnt, p->B * pl.NG, s);
        }))))
     return st;
-  return refine_lists(p, k, G, C, pl.NG, pl.chunkG, pl.list, pl.cnt, pl.mscores, pl.row_len, pl.meta,
+  return refine_lists(p, k, G, C, C, pl.NG, pl.chunkG, pl.list, pl.cnt, pl.mscores, pl.row_len, pl.meta,
                       out_idx, out_score, s);
 }
 
@@ -848,6 +860,15 @@ int idx_timer_enable(int on) {
       g_event_pool.push_back(r.b);
     }
     g_recs.clear();
+    g_dropped = 0;
+    if (on) {
+      g_recs.reserve(kTimerEvents / 2);
+      while (g_event_pool.size() < kTimerEvents) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return IDX_ERR_HIP;
+        g_event_pool.push_back(e);
+      }
+    }
     g_timer_on = on != 0;
     return IDX_OK;
   } catch (...) {
@@ -870,6 +891,7 @@ int idx_timer_read(const char* kernel_substr, double* total_ms, int32_t* launche
     }
     if (total_ms) *total_ms = tot;
     if (launches) *launches = n;
+    if (st == IDX_OK && g_dropped > 0) st = IDX_ERR_INTERNAL;   // some launches went unrecorded
     return st;
   } catch (...) {
     return IDX_ERR_INTERNAL;

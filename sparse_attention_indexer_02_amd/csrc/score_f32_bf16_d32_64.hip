@@ -1,0 +1,9 @@
+// Score kernel launchers: fp32 MFMA with bf16 keys at D=32, fp32 MFMA with bf16 keys at D=64.
+#include "score_kernel.h"
+
+namespace idx {
+
+template hipError_t launch_score_d<MmaF32, DT_BF16, 32>(const ScoreArgs&, int, hipStream_t);
+template hipError_t launch_score_d<MmaF32, DT_BF16, 64>(const ScoreArgs&, int, hipStream_t);
+
+}  // namespace idx

@@ -103,7 +103,14 @@ def test_variant_arguments(L):
     p = _problem()
     g = lambda G, C: L.idx_group_proxy_refine(ctypes.byref(p), 8, G, C, 0x50000, None, None,
                                               0x60000, 1 << 40, None)
-    assert g(0, 16) == -1 and g(4, 0) == -1 and g(4, 65) == -1
+    assert g(0, 16) == -1 and g(4, 0) == -1
+    # more candidates than the cache holds is valid: a proxy keeps at most its prefix, so the
+    # workspace is that of n_cand = N (the GPU test shows the result equals the dense indexer's)
+    gs = lambda G, C, ws_bytes: L.idx_group_proxy_refine(ctypes.byref(p), 8, G, C, 0x50000, None,
+                                                         None, 0x60000, ws_bytes, None)
+    assert gs(4, 2 * p.N, 100) == -4
+    assert L.idx_workspace_bytes(idx.OP_GROUP, ctypes.byref(p), 8, 4, 2 * p.N) == \
+        L.idx_workspace_bytes(idx.OP_GROUP, ctypes.byref(p), 8, 4, p.N) > 0
     b = lambda Bs, keep, pp=p: L.idx_block_coarse_refine(ctypes.byref(pp), 8, Bs, keep, 0x50000,
                                                          None, None, 0x60000, 1 << 40, None)
     assert b(0, 4) == -1 and b(16, 0) == -1

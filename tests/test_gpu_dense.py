@@ -98,6 +98,26 @@ def test_degenerate_cases():
     assert (gi[1, 30:35, :31] >= 0).all()
 
 
+def test_empty_tiles_write_padding():
+    # whole 8-query tiles with empty prefixes (q_pos < 0, and a sequence with an empty cache): the
+    # self-selecting score kernel must still write -1 / -inf rows over a pre-filled sentinel
+    p = W.make_prefill(96, 64, 128, seed=41, B=2)
+    p.q_pos[0, :16] = -1
+    p.k_len[1] = 0
+    k = 64
+    say("case empty tiles: q_pos[0,:16] = -1, k_len[1] = 0, bf16 self-selecting path")
+    t = dev(p)
+    oi = torch.full((2, 96, k), 12345, dtype=torch.int32, device="cuda")
+    osc = torch.full((2, 96, k), 7.0, dtype=torch.float32, device="cuda")
+    idx.score_topk(t["q"], t["k"], t["w"], t["q_pos"], topk=k, k_len=t["k_len"], out_idx=oi,
+                   out_score=osc)
+    torch.cuda.synchronize()
+    gi, gs = oi.cpu().numpy(), osc.cpu().numpy()
+    assert (gi[0, :16] == -1).all() and np.isneginf(gs[0, :16]).all()
+    assert (gi[1] == -1).all() and np.isneginf(gs[1]).all()
+    check_rows(p, k, gi, gs, [(0, t_) for t_ in range(16, 96)], "empty-tiles")
+
+
 def test_exact_ties_keep_lowest_slots():
     p = W.make_prefill(1500, 64, 128, seed=21)
     p.k[0, 300:] = np.tile(p.k[0, :100], (12, 1))    # key 300 + 100 j + i repeats key i: equal scores

@@ -77,6 +77,24 @@ def test_group_full_candidates_is_dense():
                         p.D, ctx=f"full-cand t{t}", oracle_sel=r["ids"])
 
 
+def test_group_more_candidates_than_cache_is_dense():
+    # n_cand = 2N: each proxy keeps its whole prefix, so the result equals the dense indexer's,
+    # and out_cand rows hold the prefix in ascending order, then -1 up to n_cand
+    p = W.make_prefill(250, 16, 64, seed=25)
+    C = 2 * p.N
+    say("case group with n_cand = 2N (clamped to each proxy's prefix; must equal dense)")
+    gi, gs, gc = run_group(p, 32, 8, C)
+    assert gc.shape[-1] == C
+    inp = oracle.Inputs(p)
+    for g in range(gc.shape[1]):
+        P = inp.P(0, min(p.T, 8 * g + 8) - 1)
+        assert np.array_equal(gc[0, g, :P], np.arange(P)) and (gc[0, g, P:] == -1).all()
+    for t in range(p.T):
+        r = oracle.dense_row(inp, 0, t, 32)
+        check_selection(gi[0, t], gs[0, t], r["universe"], r["all_scores"], r["magnitude"], 32,
+                        p.D, ctx=f"cand-2N t{t}", oracle_sel=r["ids"])
+
+
 def test_group_fp32_and_fp8_inputs():
     for qd, kd in ((W.F32, W.F32), (W.BF16, W.FP8_E4M3)):
         p = W.make_prefill(150, 8, 32, seed=24, q_dtype=qd, k_dtype=kd)
