@@ -90,6 +90,22 @@ typedef struct idx_problem {
 int idx_score_topk(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* idx_score_topk without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and errors as idx_score_topk, except that the
+ * scratch is the library's own static device array of 256 MiB per device (held from the
+ * library's first call on a device until the process ends; its address is looked up once per
+ * device). Prefill-shaped problems hold their score rows in chunks that fit it; decode-shaped
+ * problems need B*T*N*16 bytes plus a little, so decode calls up to about 16M cached (query,
+ * key) slots fit (e.g. 32 sequences x 2 MTP queries x 131072 keys). A problem whose plan does
+ * not fit (a single prefill row of more than about 64M keys, or a larger decode batch) returns
+ * IDX_ERR_WORKSPACE before anything is enqueued. Every call on a device shares that device's
+ * array: calls that overlap on one device (different streams, or several host threads) race and
+ * must be serialised by the caller. The array's contents persist between calls; the kernels
+ * read nothing from it that the same call did not write first. */
+int idx_score_topk_noalloc(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
+                           void* stream);
+
 /* Group-shared scan with per-query refine ("PIVOT ...", abstract; PIVOT-Refine).
  * Queries are cut into groups of `group_size` consecutive queries (the last group may be
  * shorter). Each group is reduced to one proxy query: the element-wise mean of its queries and

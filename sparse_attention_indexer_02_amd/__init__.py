@@ -26,13 +26,14 @@ from typing import Optional
 
 import torch
 
-__all__ = ["F32", "BF16", "FP8_E4M3", "IdxError", "lib", "score_topk", "group_proxy_refine",
+__all__ = ["F32", "BF16", "FP8_E4M3", "IdxError", "lib", "score_topk", "score_topk_noalloc",
+           "group_proxy_refine",
            "block_coarse_refine", "refine_given", "group_proxy_reuse", "group_block_refine", "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OP_SCORE_TOPK, OP_GROUP, OP_BLOCK, OP_REFINE, OP_REUSE = 0, 1, 2, 3, 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidx.so")
-EXPORTS = ["idx_score_topk", "idx_group_proxy_refine", "idx_block_coarse_refine",
+EXPORTS = ["idx_score_topk", "idx_score_topk_noalloc", "idx_group_proxy_refine", "idx_block_coarse_refine",
            "idx_refine_given", "idx_group_proxy_reuse", "idx_group_block_refine",
            "idx_group_block_workspace_bytes", "idx_workspace_bytes", "idx_strerror", "idx_timer_enable", "idx_timer_read"]
 
@@ -63,6 +64,7 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER(Problem)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         L.idx_score_topk.argtypes = [P, i32, vp, vp, vp, sz, vp]
+        L.idx_score_topk_noalloc.argtypes = [P, i32, vp, vp, vp]
         L.idx_group_proxy_refine.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.idx_block_coarse_refine.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.idx_refine_given.argtypes = [P, i32, i32, vp, vp, i32, vp, vp, vp, sz, vp]
@@ -77,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.idx_timer_enable.argtypes = [ctypes.c_int]
         L.idx_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int32)]
-        for f in ("idx_score_topk", "idx_group_proxy_refine", "idx_block_coarse_refine",
+        for f in ("idx_score_topk", "idx_score_topk_noalloc", "idx_group_proxy_refine", "idx_block_coarse_refine",
                   "idx_refine_given", "idx_group_proxy_reuse", "idx_group_block_refine",
                   "idx_timer_enable", "idx_timer_read"):
             getattr(L, f).restype = ctypes.c_int
@@ -176,6 +178,18 @@ def score_topk(q, k, w, q_pos, topk: int = 2048, k_len=None, k_scale=None, out_i
     _check(lib().idx_score_topk(ctypes.byref(p), topk, _ptr(out_idx), _ptr(out_score),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(q, stream)),
            "idx_score_topk")
+    return out_idx, out_score
+
+
+def score_topk_noalloc(q, k, w, q_pos, topk: int = 2048, k_len=None, k_scale=None, out_idx=None,
+                       out_score=None, stream=None):
+    """Dense lightning indexer on the library's static scratch (idx_score_topk_noalloc): the
+    outputs must be passed in for an allocation-free call."""
+    p = make_problem(q, k, w, q_pos, k_len, k_scale)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, True)
+    _check(lib().idx_score_topk_noalloc(ctypes.byref(p), topk, _ptr(out_idx), _ptr(out_score),
+                                        _stream(q, stream)),
+           "idx_score_topk_noalloc")
     return out_idx, out_score
 
 

@@ -3,6 +3,7 @@
 // synchronisation). See include/idx.h for the contract.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -126,10 +127,12 @@ struct DensePlan {
   size_t bytes;
 };
 
-DensePlan plan_dense(const idx_problem* p, void* ws) {
+// score rows are held in chunks of at most `row_budget` bytes
+DensePlan plan_dense(const idx_problem* p, void* ws, size_t row_budget = kScoreBudget) {
   DensePlan d;
   Carver c(ws);
-  d.chunkT = chunk_rows(p->B, rstride(p->N) * 4, p->T);
+  d.chunkT = (int)std::max<int64_t>(
+      1, std::min<int64_t>(p->T, (int64_t)row_budget / std::max<int64_t>(1, (int64_t)p->B * rstride(p->N) * 4)));
   d.scores = c.take<float>((size_t)p->B * d.chunkT * rstride(p->N));
   d.row_len = c.take<int32_t>((size_t)p->B * d.chunkT);
   d.meta = c.take<int32_t>((size_t)p->B * d.chunkT * 4);
@@ -379,13 +382,13 @@ int decode_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_sc
 }
 
 int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
-                    void* ws, size_t ws_bytes, hipStream_t s) {
+                    void* ws, size_t ws_bytes, hipStream_t s, size_t row_budget = kScoreBudget) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
   if (use_decode(p)) return decode_impl(p, k, out_idx, out_score, ws, ws_bytes, s);
-  DensePlan pl = plan_dense(p, nullptr);
+  DensePlan pl = plan_dense(p, nullptr, row_budget);
   if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
-  pl = plan_dense(p, align_ws(ws));
+  pl = plan_dense(p, align_ws(ws), row_budget);
   for (int c0 = 0; c0 < p->T; c0 += pl.chunkT) {
     const int c1 = std::min(p->T, c0 + pl.chunkT);
     ScoreArgs a = base_score_args(p);
@@ -731,6 +734,54 @@ int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_
   return IDX_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// library-owned scratch of idx_score_topk_noalloc: one static device array, whose address each
+// device's copy has is looked up once per device (the array's name is not a device address in
+// host code)
+
+constexpr size_t kStaticScratch = size_t(256) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratch];
+
+void* static_scratch(int* status) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *status = IDX_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *status = IDX_ERR_HIP;
+      return nullptr;
+    }
+    ptrs[dev] = ptr;
+  }
+  *status = IDX_OK;
+  return ptrs[dev];
+}
+
+int score_topk_noalloc_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
+                            hipStream_t s) {
+  int st = validate(p, k, out_idx, out_score);
+  if (st) return st;
+  // the plan must fit the static scratch: decode needs its whole plan, prefill chunks its rows
+  size_t budget = kStaticScratch;
+  if (use_decode(p)) {
+    if (plan_decode(p, nullptr).bytes > kStaticScratch) return IDX_ERR_WORKSPACE;
+  } else {
+    while (plan_dense(p, nullptr, budget).bytes > kStaticScratch) {
+      if (plan_dense(p, nullptr, budget).chunkT == 1) return IDX_ERR_WORKSPACE;
+      budget -= budget / 16 + 1;
+    }
+  }
+  void* ws = static_scratch(&st);
+  if (st) return st;
+  return score_topk_impl(p, k, out_idx, out_score, ws, kStaticScratch, s, budget);
+}
+
 }  // namespace
 }  // namespace idx
 
@@ -743,6 +794,15 @@ int idx_score_topk(const idx_problem* p, int32_t k, int32_t* out_idx, float* out
   try {
     return score_topk_impl(p, k, out_idx, out_score, ws, ws_bytes,
                            static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return IDX_ERR_INTERNAL;
+  }
+}
+
+int idx_score_topk_noalloc(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
+                           void* stream) {
+  try {
+    return score_topk_noalloc_impl(p, k, out_idx, out_score, static_cast<hipStream_t>(stream));
   } catch (...) {
     return IDX_ERR_INTERNAL;
   }
