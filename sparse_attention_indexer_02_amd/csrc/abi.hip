@@ -109,10 +109,10 @@ int chunk_rows(int B, int64_t row_bytes, int rows) {
   return (int)c;
 }
 
-// split of the key range so that a launch has about kTargetGroups work-groups
-int key_split(int n_groups, int n_keys, int* split_keys) {
+// split of the key range so that a launch has about `target` work-groups
+int key_split(int n_groups, int n_keys, int* split_keys, int target = kTargetGroups) {
   int splits = 1;
-  if (n_groups < kTargetGroups) splits = (kTargetGroups + n_groups - 1) / n_groups;
+  if (n_groups < target) splits = (target + n_groups - 1) / n_groups;
   int sk = (n_keys + splits - 1) / splits;
   sk = std::max(KEY_TILE * 4, (sk + KEY_TILE - 1) / KEY_TILE * KEY_TILE);
   *split_keys = sk;
@@ -325,19 +325,23 @@ ScoreArgs base_score_args(const idx_problem* p) {
 
 // Launches the score kernel; when the key range is not split, the kernel also writes each row's
 // selection summary into `meta` for the selector, and *fused is set.
+// `target` is the work-group count below which the key range is split (a split range gives no
+// row summary, so the self-selecting dense rows only split when the launch cannot cover the CUs).
 hipError_t run_score(ScoreArgs& a, int n_keys_max, int topk_k, int32_t* meta, bool* fused,
-                     hipStream_t s) {
+                     hipStream_t s, int target = kTargetGroups) {
   const int qt = score_queries_per_tile(a.H);
   if (a.mode == MODE_RANGE) {
     a.tiles_per_seq = (a.c1 - a.c0 + qt - 1) / qt;
   } else {
     a.tiles_per_seq = (a.c1 - a.c0) * ((a.group_size + qt - 1) / qt);
   }
-  const int nsplit = key_split(a.B * a.tiles_per_seq, n_keys_max, &a.split_keys);
+  const int nsplit = key_split(a.B * a.tiles_per_seq, n_keys_max, &a.split_keys, target);
   *fused = nsplit == 1 && meta != nullptr;
   a.row_meta = *fused ? meta : nullptr;
   a.topk_k = topk_k;
-  a.digit_bits = n_keys_max < 65536 ? 12 : 11;
+  // 12-bit digits count in 16-bit halves, which rows of up to 65536 slots fit (the score kernel
+  // keeps slot 65535 out of the counters)
+  a.digit_bits = n_keys_max <= 65536 ? 12 : 11;
   return timed("score", s, [&] { return launch_score(a, nsplit, s); });
 }
 
@@ -395,13 +399,14 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
     a.c0 = c0; a.c1 = c1;
     a.scores = pl.scores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
-    // bf16 rows shorter than 64K slots: each score-kernel wave selects its own row
-    const bool self_select = p->q_dtype == IDX_BF16 && p->k_dtype == IDX_BF16 && p->N < 65536;
+    // bf16 rows of up to 65536 slots: each score-kernel wave selects its own row
+    const bool self_select = p->q_dtype == IDX_BF16 && p->k_dtype == IDX_BF16 && p->N <= 65536;
     if (self_select) {
       a.sel_idx = out_idx; a.sel_score = out_score; a.sel_T = p->T;
     }
     bool fused;
-    if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s)))) return st;
+    if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s, self_select ? cu_count() : kTargetGroups))))
+      return st;
     if (fused && self_select) continue;
     TopkArgs t = topk_args(pl.scores, rstride(p->N), pl.row_len, p->B * (c1 - c0), k, c1 - c0, p->T, c0,
                            out_idx, out_score, k);

@@ -24,19 +24,25 @@ template <class Mma, int KST> struct TileKeys {
   static constexpr int value = Direct<Mma, KST>::value ? 128 : 64;
 };
 
-// One wave selects the top k slots of its own score row (n slots) from the row's 12-bit
+// One wave selects the top k slots of its own score row (n <= 65536 slots) from the row's 12-bit
 // first-digit summary: tot finite slots, bin b1 of the k-th largest key, `above` slots in higher
-// bins and `inbin` slots in bin b1. Pass 1 over the row writes the slots above bin b1 and keeps
-// the slots of bin b1: when they fit (inbin <= CAP) as (key, slot) pairs in LDS (keys in `ck`,
-// 16-bit slots in the upper half of `h`), otherwise as a histogram of their next 10 key bits. The
-// k-th key is then resolved digit by digit: 10 more bits give its 22-bit prefix; slots above the
-// prefix are written, and the slots sharing it (at most 256) are ranked exactly, higher key first,
-// then lower slot (ties keep the lowest slots); a prefix shared by more slots takes a last 10-bit
-// digit and keeps the lowest slots equal to the k-th key. Histograms use 1024 words of `h`. Without
-// the LDS copy the row is read again from global memory for each step. Row reads are eight
-// 16-byte loads per lane at a time. Output order: pass order, slot order within a pass.
+// bins and `inbin` slots in bin b1. One pass over the row writes the slots above bin b1 to the
+// output and keeps the slots of bin b1:
+//   - when they fit (inbin <= CAP) as (key, slot) pairs in LDS (keys in `ck`, 16-bit slots in the
+//     upper half of `h`);
+//   - otherwise compacted into the row itself: entry p (written over slot p, which this wave has
+//     already read, since p counts a subset of the slots read so far) holds the key's low 20 bits
+//     and the slot's low 12 bits; the slot's upper bits come from a table of the entry count
+//     before each 4096-slot block (h[1024..1041)), and the key's upper 12 bits are b1. The 10-bit
+//     histogram of the next digit is built during the pass.
+// The k-th key is then resolved on the kept slots digit by digit: 10 more bits give its 22-bit
+// prefix; slots above the prefix are written, and the slots sharing it (at most 256) are ranked
+// exactly, higher key first, then lower slot (ties keep the lowest slots); a prefix shared by more
+// slots takes a last 10-bit digit and keeps the lowest slots equal to the k-th key. Histograms use
+// 1024 words of `h`. Row reads are eight 16-byte loads per lane at a time. Output order: pass
+// order, slot order within a pass.
 template <int CAP>
-__device__ __forceinline__ void wave_select_row(const float* srow, int n, int64_t stride, int k,
+__device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stride, int k,
                                                 uint32_t tot, int b1, uint32_t above, uint32_t inbin,
                                                 uint32_t* h, uint32_t* ck, int32_t* oidx, float* osc) {
   static_assert(CAP <= 2048, "16-bit slots in 1024 words");
@@ -44,8 +50,12 @@ __device__ __forceinline__ void wave_select_row(const float* srow, int n, int64_
   const int lane = lane_id();
   const uint32_t kk = min((uint32_t)k, tot);
   const bool all = kk == tot;
-  const bool gather = !all && inbin <= (uint32_t)CAP;
+  const bool lds = !all && inbin <= (uint32_t)CAP;   // bin b1 kept as LDS pairs
+  const bool glob = !all && !lds;                     // bin b1 compacted into the row
   uint16_t* cs = reinterpret_cast<uint16_t*>(h + 1024);
+  uint32_t* blk = h + 1024;                           // glob: entries before each 4096-slot block
+  uint32_t* crow = reinterpret_cast<uint32_t*>(srow);
+  const int nblk = (n + 4095) >> 12;
   const int last = (int)stride - 4;
   // visits the row 256 slots at a time: f(i0, key[4], v) with key 0 past the row
   auto stream = [&](auto f) {
@@ -110,8 +120,8 @@ __device__ __forceinline__ void wave_select_row(const float* srow, int n, int64_
     }
   };
   const uint32_t ub1 = (uint32_t)b1;
-  if (!all && !gather) zero_hist();
-  uint32_t cb = 0;                                       // gathered slots
+  if (glob) zero_hist();
+  uint32_t cb = 0;                                       // kept slots of bin b1
   stream([&](int i0, const uint32_t (&key)[4], const f32x4_t& v) {
     bool sel[4];
     uint32_t ce = 0;
@@ -120,7 +130,7 @@ __device__ __forceinline__ void wave_select_row(const float* srow, int n, int64_
       sel[e] = all ? key[e] > KEY_NEG_INF : (key[e] >> 20) > ub1;
       ce += (key[e] >> 20) == ub1 ? 1u : 0u;
     }
-    if (gather) {
+    if (lds) {
       const uint32_t einc = wave_scan_dpp(ce);
       uint32_t p = cb + einc - ce;
 #pragma unroll
@@ -132,18 +142,49 @@ __device__ __forceinline__ void wave_select_row(const float* srow, int n, int64_
         p += (key[e] >> 20) == ub1 ? 1u : 0u;
       }
       cb += wave_bcast(einc, 63);
-    } else if (!all) {
+    } else if (glob) {
+      if ((i0 & 4095) == 0 && lane == 0) blk[i0 >> 12] = cb;
+      const uint32_t einc = wave_scan_dpp(ce);
+      uint32_t p = cb + einc - ce;                       // p < i0 + 256: slots already read
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((key[e] >> 20) == ub1) atomicAdd(&h[(key[e] >> 10) & 0x3FFu], 1u);
+      for (int e = 0; e < 4; ++e) {
+        if ((key[e] >> 20) == ub1) {
+          crow[p] = ((key[e] & 0xFFFFFu) << 12) | ((uint32_t)(i0 + 4 * lane + e) & 0xFFFu);
+          atomicAdd(&h[(key[e] >> 10) & 0x3FFu], 1u);
+        }
+        p += (key[e] >> 20) == ub1 ? 1u : 0u;
+      }
+      cb += wave_bcast(einc, 63);
     }
     emit(i0, sel, v);
   });
   if (!all) {
+    if (glob) {
+      if (lane == 0) blk[nblk] = cb;
+      // the compacted entries are read back: wait for the stores, and drop any stale copy of
+      // the row the vector L1 cache still holds
+      wait_vmem();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    // kept slot i of bin b1: its key and slot
+    auto get = [&](int i, uint32_t& key, uint32_t& slot) {
+      if (lds) {
+        key = ck[i];
+        slot = cs[i];
+      } else {
+        const uint32_t e = crow[i];
+        int j = 0;                                       // block j: blk[j] <= i < blk[j + 1]
+#pragma unroll
+        for (int st = 8; st > 0; st >>= 1)
+          if (j + st < nblk && blk[j + st] <= (uint32_t)i) j += st;
+        key = (ub1 << 20) | (e >> 12);
+        slot = ((uint32_t)j << 12) | (e & 0xFFFu);
+      }
+    };
     uint32_t need = kk - above;
     int b2, b3;
     uint32_t ab;
-    if (gather) {
+    if (lds) {
       zero_hist();
       for (int i = lane; i < (int)inbin; i += 64) atomicAdd(&h[(ck[i] >> 10) & 0x3FFu], 1u);
     }
@@ -151,91 +192,42 @@ __device__ __forceinline__ void wave_select_row(const float* srow, int n, int64_
     need -= ab;
     const uint32_t pre = (ub1 << 10) | (uint32_t)b2;
     const uint32_t c2 = h[b2];                           // slots sharing the 22-bit prefix
-    if (gather) {
-      if (c2 <= 256) {
-        uint32_t eb = 0;
-        for (int i0 = 0; i0 < (int)inbin; i0 += 64) {
-          const int i = i0 + lane;
-          const uint32_t key = i < (int)inbin ? ck[i] : 0u;
-          const uint32_t slot = i < (int)inbin ? cs[i] : 0u;
-          const bool eq = (key >> 10) == pre;
-          const uint32_t einc = wave_scan_dpp(eq ? 1u : 0u);
-          if (eq) {
-            h[eb + einc - 1] = key;
-            h[256 + eb + einc - 1] = slot;
-          }
-          eb += wave_bcast(einc, 63);
-          emit1((key >> 10) > pre, slot, key);
-        }
-        rank_emit(c2, need);
-      } else {
-        zero_hist();
-        for (int i = lane; i < (int)inbin; i += 64)
-          if ((ck[i] >> 10) == pre) atomicAdd(&h[ck[i] & 0x3FFu], 1u);
-        wave_hist_find(1024, need, [&](int q) { return h[q]; }, &b3, &ab);
-        const uint32_t T = (pre << 10) | (uint32_t)b3;
-        const uint32_t need_eq = need - ab;              // slots equal to T that are kept
-        uint32_t eqb = 0;
-        for (int i0 = 0; i0 < (int)inbin; i0 += 64) {
-          const int i = i0 + lane;
-          const uint32_t key = i < (int)inbin ? ck[i] : 0u;
-          const uint32_t slot = i < (int)inbin ? cs[i] : 0u;
-          const bool eq = key == T;
-          const uint32_t einc = wave_scan_dpp(eq ? 1u : 0u);
-          emit1(key > T || (eq && eqb + einc - 1 < need_eq), slot, key);
-          eqb += wave_bcast(einc, 63);
-        }
-      }
-    } else if (c2 <= 256) {
+    if (c2 <= 256) {
       uint32_t eb = 0;
-      stream([&](int i0, const uint32_t (&key)[4], const f32x4_t& v) {
-        bool sel[4];
-        uint32_t ce = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sel[e] = (key[e] >> 20) == ub1 && (key[e] >> 10) > pre;
-          ce += (key[e] >> 10) == pre ? 1u : 0u;
-        }
-        const uint32_t einc = wave_scan_dpp(ce);
-        uint32_t p = eb + einc - ce;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((key[e] >> 10) == pre && p < 256u) {
-            h[p] = key[e];
-            h[256 + p] = (uint32_t)(i0 + 4 * lane + e);
-          }
-          p += (key[e] >> 10) == pre ? 1u : 0u;
+      for (int i0 = 0; i0 < (int)inbin; i0 += 64) {
+        const int i = i0 + lane;
+        uint32_t key = 0, slot = 0;
+        if (i < (int)inbin) get(i, key, slot);
+        const bool eq = (key >> 10) == pre;
+        const uint32_t einc = wave_scan_dpp(eq ? 1u : 0u);
+        if (eq) {
+          h[eb + einc - 1] = key;
+          h[256 + eb + einc - 1] = slot;
         }
         eb += wave_bcast(einc, 63);
-        emit(i0, sel, v);
-      });
+        emit1((key >> 10) > pre, slot, key);
+      }
       rank_emit(c2, need);
     } else {
       zero_hist();
-      stream([&](int, const uint32_t (&key)[4], const f32x4_t&) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((key[e] >> 10) == pre) atomicAdd(&h[key[e] & 0x3FFu], 1u);
-      });
+      for (int i = lane; i < (int)inbin; i += 64) {
+        uint32_t key, slot;
+        get(i, key, slot);
+        if ((key >> 10) == pre) atomicAdd(&h[key & 0x3FFu], 1u);
+      }
       wave_hist_find(1024, need, [&](int q) { return h[q]; }, &b3, &ab);
       const uint32_t T = (pre << 10) | (uint32_t)b3;
       const uint32_t need_eq = need - ab;                // slots equal to T that are kept
-      uint32_t eqb = 0;                                  // equal slots seen so far
-      stream([&](int i0, const uint32_t (&key)[4], const f32x4_t& v) {
-        const uint32_t ce = (key[0] == T ? 1u : 0u) + (key[1] == T ? 1u : 0u) + (key[2] == T ? 1u : 0u) +
-                            (key[3] == T ? 1u : 0u);
-        const uint32_t einc = wave_scan_dpp(ce);
-        uint32_t r = eqb + einc - ce;                    // rank of this lane's first equal slot
-        bool sel[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool eq = key[e] == T;
-          sel[e] = ((key[e] >> 20) == ub1 && key[e] > T) || (eq && r < need_eq);
-          r += eq ? 1u : 0u;
-        }
+      uint32_t eqb = 0;
+      for (int i0 = 0; i0 < (int)inbin; i0 += 64) {
+        const int i = i0 + lane;
+        uint32_t key = 0, slot = 0;
+        if (i < (int)inbin) get(i, key, slot);
+        const bool eq = key == T;
+        const uint32_t einc = wave_scan_dpp(eq ? 1u : 0u);
+        emit1(key > T || (eq && eqb + einc - 1 < need_eq), slot, key);
         eqb += wave_bcast(einc, 63);
-        emit(i0, sel, v);
-      });
+      }
     }
   }
   for (int p = (int)kk + lane; p < k; p += 64) {
@@ -449,6 +441,9 @@ score_kernel(ScoreArgs a) {
   // first load: the compiler waits for every outstanding vector memory operation before an LDS
   // access that follows the tiles' LDS loads, so the histogram adds must not come after a
   // load; and at the end of the tile they would hold every wave up at the tile barrier.
+  // 12-bit digits count in 16-bit halves: slot 65535 (only rows of 65536 slots have it) is kept
+  // out of the histogram so that no count reaches 65536; the summary adds it back
+  const int xslot = a.digit_bits == 12 ? 65535 : -1;
   float pv[NSUB / 2];
   int pbase = -1;                                     // first slot of the pending scores, or -1
 #pragma unroll
@@ -461,7 +456,7 @@ score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int p = 0; p < NSUB / 2; ++p) {
           const uint32_t key = f2key(pv[p]);
-          hist1_add_if(whist, key, a.digit_bits, key > KEY_NEG_INF);
+          hist1_add_if(whist, key, a.digit_bits, key > KEY_NEG_INF && pbase + p * 64 + lane != xslot);
         }
       }
 #pragma unroll
@@ -598,7 +593,7 @@ score_kernel(ScoreArgs a) {
           }
           if (fuse) {
             const uint32_t key = f2key(v[p]);
-            if (key > KEY_NEG_INF) hist1_add(whist, key, a.digit_bits);
+            if (key > KEY_NEG_INF && base + n != xslot) hist1_add(whist, key, a.digit_bits);
           }
         }
       }
@@ -613,26 +608,33 @@ score_kernel(ScoreArgs a) {
     int bin;
     uint32_t above;
     const int bits = a.digit_bits;
+    wait_vmem();                                         // this wave's score stores
+    // the bin of slot 65535's key, which the histogram left out (-1 if none)
+    int xbin = -1;
+    if (lim > xslot && xslot >= 0) {
+      const uint32_t xk = f2key(srow[xslot]);
+      if (xk > KEY_NEG_INF) xbin = (int)digit1(xk, bits);
+    }
     // bin q's count without a branch on the digit width (12 bits: bins q and q + 2048 are the
     // 16-bit halves of word q mod 2048)
     const uint32_t hm = bits == 12 ? 0xFFFFu : 0xFFFFFFFFu;
     const int hsh = bits == 12 ? 11 : 31;
-    const uint32_t tot = wave_hist_find(1 << bits, (uint32_t)a.topk_k,
-                                        [&](int q) { return (whist[q & 2047] >> ((q >> hsh) << 4)) & hm; },
-                                        &bin, &above);
+    const uint32_t tot = wave_hist_find(
+        1 << bits, (uint32_t)a.topk_k,
+        [&](int q) { return ((whist[q & 2047] >> ((q >> hsh) << 4)) & hm) + (q == xbin ? 1u : 0u); }, &bin,
+        &above);
+    const uint32_t inbin = bin >= 0 ? hist1_count(whist, bin, bits) + (bin == xbin ? 1u : 0u) : 0u;
     if (lane == 0) {
       int32_t* m = a.row_meta + ((int64_t)b * a.rows_per_seq + (t - row0)) * 4;
       m[META_NVALID] = (int32_t)tot;
       m[META_BIN] = bin;
       m[META_ABOVE] = (int32_t)above;
-      m[META_INBIN] = bin >= 0 ? (int32_t)hist1_count(whist, bin, bits) : 0;
+      m[META_INBIN] = (int32_t)inbin;
     }
     if constexpr (!LISTM) {
       if (a.sel_idx != nullptr && bits == 12) {
-        wait_vmem();                                     // this wave's score stores
         // the wave's share of the key tiles (idle after the last tile) holds bin b1's keys
         constexpr int SLICE = 2 * G::TILE_BYTES / NW / 4;
-        const uint32_t inbin = bin >= 0 ? hist1_count(whist, bin, 12) : 0u;
         wave_select_row<SLICE < 2048 ? SLICE : 2048>(
             srow, my_count, a.score_stride, a.topk_k, tot, bin, above, inbin, whist,
             reinterpret_cast<uint32_t*>(tiles + wave * (2 * G::TILE_BYTES / NW)),

@@ -137,8 +137,8 @@ def test_exact_ties_keep_lowest_slots():
 
 
 def test_long_rows_wide_boundary_bin():
-    # D=64: the boundary bin of these rows holds more slots than the selector keeps on chip, so
-    # the selection reads the row again for each digit; the all-zero rows also tie at the k-th key
+    # D=64: the boundary bin of these rows holds more slots than the selector keeps in LDS, so
+    # they are compacted into the score row; the all-zero rows also tie at the k-th key
     p = W.make_prefill(24000, 8, 64, seed=31)
     p.w[0, 22000:22003] = 0.0
     k = 2048
@@ -176,8 +176,11 @@ def test_dense16k_full_size_sampled_rows():
     p = spec["gen"](0)
     say("case dense16k full size (L=16384, H=64, D=128, k=2048)")
     gi, gs = run_dense(p, spec["k"])
+    # 128 rows spread over the causal triangle (one per 128-row stratum, at varying offsets in
+    # the 8-query tile) plus the tile and k boundaries
     rng = np.random.default_rng(0)
-    ts = sorted(set([0, 1, 2047, 2048, 2049, 8191, 16383] + list(rng.integers(0, 16384, 25))))
+    ts = sorted(set([0, 1, 7, 8, 2046, 2047, 2048, 2049, 8191, 8192, 16383] +
+                    [128 * j + int(rng.integers(0, 128)) for j in range(128)]))
     flips = check_rows(p, spec["k"], gi, gs, [(0, t) for t in ts], "dense16k")
     say(f"dense16k: {len(ts)} rows checked, {flips} tie-band swaps")
     # structure of every row: count = min(k, t+1), ascending, causal
@@ -188,19 +191,38 @@ def test_dense16k_full_size_sampled_rows():
 
 @pytest.mark.timeout(1200)
 def test_dense64k_full_size_sampled_rows():
-    # rows of 64K keys: 11-bit first digits in the score kernel's summary and the separate
-    # stream selector, whose boundary bin no longer fits on chip for the longest rows
+    # rows of up to 65536 keys, selected by the score kernel's own waves (12-bit first digits,
+    # boundary bins beyond the LDS copy compacted into the score row); the rows are scored in
+    # chunks of 4096 queries, so both sides of every chunk boundary are checked
     spec = W.WORKLOADS["dense64k"]
     p = spec["gen"](0)
     say("case dense64k full size (L=65536, H=64, D=128, k=2048)")
     gi, gs = run_dense(p, spec["k"])
     rng = np.random.default_rng(1)
-    ts = sorted(set([0, 2047, 2048, 32767, 65535] + list(rng.integers(0, 65536, 7))))
+    ts = sorted(set([0, 2047, 2048, 32767, 65535] + [4096 * j + d for j in range(1, 16) for d in (-1, 0)] +
+                    list(rng.integers(0, 65536, 7))))
     flips = check_rows(p, spec["k"], gi, gs, [(0, t) for t in ts], "dense64k")
     say(f"dense64k: {len(ts)} rows checked, {flips} tie-band swaps")
     cnt = (gi[0] >= 0).sum(-1)
     assert np.array_equal(cnt, np.minimum(spec["k"], np.arange(65536) + 1))
     assert (gi[0].max(-1) <= np.arange(65536)).all()
+
+
+@pytest.mark.timeout(600)
+def test_rows_of_65536_slots_with_equal_scores():
+    # the last tile's rows have all-zero head weights, so every score is 0: row 65535 puts all
+    # 65536 slots into one bin of the 16-bit-half histogram (slot 65535 is counted outside it),
+    # and the selection keeps the 2048 lowest slots of the tie; D=64 keeps fewer boundary slots in
+    # LDS, so the other long rows take the compacted-row path
+    p = W.make_prefill(65536, 8, 64, seed=61)
+    p.w[0, 65528:] = 0.0
+    k = 2048
+    say("case rows of 65536 slots: L=65536 H=8 D=64 k=2048, last tile all-zero weights")
+    gi, gs = run_dense(p, k)
+    for t in range(65528, 65536):
+        assert set(gi[0, t].tolist()) == set(range(k)), f"equal-65536 t{t}"
+        assert (gs[0, t] == 0).all()
+    check_rows(p, k, gi, gs, [(0, t) for t in (2047, 4095, 4096, 40000, 65000, 65527, 65535)], "rows-65536")
 
 
 @pytest.mark.timeout(900)
