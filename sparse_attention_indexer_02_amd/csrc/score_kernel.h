@@ -57,13 +57,18 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
   uint32_t* crow = reinterpret_cast<uint32_t*>(srow);
   const int nblk = (n + 4095) >> 12;
   const int last = (int)stride - 4;
-  // visits the row 256 slots at a time: f(i0, key[4], v) with key 0 past the row
+  // visits the row 256 slots at a time: f(i0, key[4], v) with key 0 past the row. The loads of
+  // the next 256 U slots are in flight while the current ones are processed (two register
+  // buffers); addresses are clamped into the row's allocation. f may overwrite slots below the
+  // end of the block it processes: the loads in flight are all at or above it.
   auto stream = [&](auto f) {
-    for (int i0 = 0; i0 < n; i0 += 256 * U) {
-      f32x4_t v[U];
+    f32x4_t va[U], vb[U];
+    auto load = [&](int i0, f32x4_t (&v)[U]) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
         v[u] = *reinterpret_cast<const f32x4_t*>(srow + min(i0 + 256 * u + 4 * lane, last));
+    };
+    auto run = [&](int i0, const f32x4_t (&v)[U]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j0 = i0 + 256 * u;
@@ -73,17 +78,26 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
         for (int e = 0; e < 4; ++e) key[e] = j0 + 4 * lane + e < n ? f2key(v[u][e]) : 0u;
         f(j0, key, v[u]);
       }
+    };
+    load(0, va);
+    for (int i0 = 0; i0 < n; i0 += 512 * U) {
+      load(i0 + 256 * U, vb);
+      run(i0, va);
+      if (i0 + 256 * U >= n) break;
+      load(i0 + 512 * U, va);
+      run(i0 + 256 * U, vb);
     }
   };
   uint32_t pos = 0;
-  // writes the slots flagged in sel[4] at pos, in slot order
+  // writes the slots flagged in sel[4] at pos, in slot order (never past the k outputs, whatever
+  // the summary says)
   auto emit = [&](int i0, const bool (&sel)[4], const f32x4_t& v) {
     const uint32_t c = (sel[0] ? 1u : 0u) + (sel[1] ? 1u : 0u) + (sel[2] ? 1u : 0u) + (sel[3] ? 1u : 0u);
     const uint32_t inc = wave_scan_dpp(c);
     uint32_t p = pos + inc - c;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (sel[e]) {
+      if (sel[e] && p < (uint32_t)k) {
         oidx[p] = i0 + 4 * lane + e;
         if (osc) osc[p] = v[e];
       }
@@ -94,7 +108,7 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
   // writes one flagged slot per lane at pos, in lane order
   auto emit1 = [&](bool sel, uint32_t slot, uint32_t key) {
     const uint32_t inc = wave_scan_dpp(sel ? 1u : 0u);
-    if (sel) {
+    if (sel && pos + inc - 1 < (uint32_t)k) {
       oidx[pos + inc - 1] = (int32_t)slot;
       if (osc) osc[pos + inc - 1] = key2f(key);
     }
@@ -148,7 +162,7 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
       uint32_t p = cb + einc - ce;                       // p < i0 + 256: slots already read
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if ((key[e] >> 20) == ub1) {
+        if ((key[e] >> 20) == ub1 && p < (uint32_t)n) {
           crow[p] = ((key[e] & 0xFFFFFu) << 12) | ((uint32_t)(i0 + 4 * lane + e) & 0xFFFu);
           atomicAdd(&h[(key[e] >> 10) & 0x3FFu], 1u);
         }
@@ -181,6 +195,7 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
         slot = ((uint32_t)j << 12) | (e & 0xFFFu);
       }
     };
+    inbin = min(inbin, min(cb, lds ? (uint32_t)CAP : (uint32_t)n));   // slots actually kept
     uint32_t need = kk - above;
     int b2, b3;
     uint32_t ab;
@@ -200,7 +215,7 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
         if (i < (int)inbin) get(i, key, slot);
         const bool eq = (key >> 10) == pre;
         const uint32_t einc = wave_scan_dpp(eq ? 1u : 0u);
-        if (eq) {
+        if (eq && eb + einc - 1 < 256u) {
           h[eb + einc - 1] = key;
           h[256 + eb + einc - 1] = slot;
         }
@@ -465,6 +480,27 @@ score_kernel(ScoreArgs a) {
     }
   };
 
+  // bf16 key ranges carry the last 32-key step of a full tile into the next tile: its epilogue
+  // runs under the MFMAs of the next tile's first step (which otherwise has no epilogue to hide)
+  // instead of after the tile's MFMAs, where both waves of a SIMD would run it at once, between
+  // two barriers. The carried tile's scores are then complete after that first step and are
+  // flushed at the start of the tile after (stores and histogram adds stay ahead of every load).
+  constexpr bool CARRY = DIRECT && !LISTM;
+  f32x16_t A[HB], Bq[HB];                             // step accumulators (Bq: the carried step)
+  bool carry = false;
+  float c_ov0 = 0.f, c_tprev = 0.f;                   // the carried tile's other scores
+  int c_base = 0;
+  auto finish_carry = [&]() {                         // carried step's epilogue without MFMAs
+    if (CARRY && carry) {
+      const float tl = tile_epilogue<HB>(Bq, wv);
+      pv[0] = c_ov0;
+      pv[1] = lane < 32 ? c_tprev : tl;
+      pbase = c_base;
+      carry = false;
+      flush();
+    }
+  };
+
   for (int it = 0; it < ntile; ++it) {
     const int cur = it & 1;
     const int base = kb0 + it * KT;
@@ -475,6 +511,7 @@ score_kernel(ScoreArgs a) {
     // issue them all here
     const bool full = active && base + KT <= lim;
     const bool spread = DIRECT && full;
+    if (!full) finish_carry();
     if (more && !spread) {
       issue_tile(cur ^ 1, base + KT);
       if constexpr (DIRECT) {
@@ -486,63 +523,55 @@ score_kernel(ScoreArgs a) {
     float ov[NSUB / 2];
 #pragma unroll
     for (int p = 0; p < NSUB / 2; ++p) ov[p] = 0.f;
-    if (full) {
-      // full tile: the epilogue of each 32-key step overlaps the MFMAs of the next one, and
-      // the next step's key fragments are read from LDS while this step's MFMAs run
-      f32x16_t A[HB], Bq[HB];
+    if (full && DIRECT) {
+      // full bf16 tile: each 32-key step's MFMAs carry the previous step's epilogue, fragment by
+      // fragment, and refill the key fragments for the next step from LDS; the next tile's load
+      // chunks go out during the first NSUB - 1 steps (chunk i in step i (NSUB - 1) / IT, at odd
+      // fragments), so that the last has a whole step to land; on the last tile they refill the
+      // idle buffer with rows already read (no branch inside the MFMA stream)
       float t_prev = 0.f;
-      auto mma_step = [&](int s, f32x16_t (&acc)[HB]) {
+      constexpr int IT = DIRECT ? DLoader::ITERS : 1;
+      auto dma = [&](int s, int kk) {
         if constexpr (DIRECT) {
-          tile_mma_rot<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, lane, acc);
-        } else {
-          tile_mma<Mma, D, HB, KT>(qf, tile, s * 32, lane, acc);
+          const int i0 = (s * IT + NSUB - 2) / (NSUB - 1);
+          const int i1 = min(IT, ((s + 1) * IT + NSUB - 2) / (NSUB - 1));
+          const int i = i0 + (kk - 1) / 2;
+          if ((kk & 1) && i < i1)
+            DLoader::load_chunk(i, kseq, tiles + (cur ^ 1) * G::TILE_BYTES, wave, lane, chunk_key(base + KT, i));
         }
       };
-      // the next tile's load chunks go out during the first NSUB - 1 steps (chunk i in step
-      // i (NSUB - 1) / IT), so that the last has a whole step to land; on the last tile they
-      // refill the idle buffer with rows already read (no branch inside the MFMA stream)
-      constexpr int IT = DIRECT ? DLoader::ITERS : 0;
-      auto dma_part = [&](int s) {
-        if constexpr (DIRECT) {
-#pragma unroll
-          for (int i = (s * IT + NSUB - 2) / (NSUB - 1); i < ((s + 1) * IT + NSUB - 2) / (NSUB - 1) && i < IT; ++i)
-            DLoader::load_chunk(i, kseq, tiles + (cur ^ 1) * G::TILE_BYTES, wave, lane,
-                                chunk_key(base + KT, i));
-        }
-      };
-      if constexpr (DIRECT) load_bfrag<D, KT>(tile, 0, lane, bfr);
-      mma_step(0, A);
-      dma_part(0);
-#pragma unroll
-      for (int s = 1; s < NSUB; ++s) {
-        float tcur;
-        if constexpr (DIRECT) __builtin_amdgcn_sched_barrier(0);
-        if (s & 1) {
-          mma_step(s, Bq);
-          tcur = tile_epilogue<HB>(A, wv);
-        } else {
-          mma_step(s, A);
-          tcur = tile_epilogue<HB>(Bq, wv);
-        }
-        dma_part(s);
-        if constexpr (DIRECT) {
-          // per key-fragment step: HB MFMAs, one LDS read of the next step, then a slice of
-          // the previous step's epilogue; this step's load chunks go out after the first MFMAs
-          constexpr int NL = IT / NSUB > 0 ? IT / NSUB : 1;
-#pragma unroll
-          for (int kk = 0; kk < G::NKK; ++kk) {
-            __builtin_amdgcn_sched_group_barrier(0x008, HB, 0);
-            if (s + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (kk == 1) __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, (16 * HB * 2 + 8) / G::NKK + 1, 0);
-          }
-        }
-        if ((s - 1) & 1) ov[(s - 2) / 2] = lane < 32 ? t_prev : tcur;
-        else t_prev = tcur;
-      }
-      const float tl = tile_epilogue<HB>(Bq, wv);
-      ov[NSUB / 2 - 1] = lane < 32 ? t_prev : tl;
       if constexpr (DIRECT) {
+        static_assert(NSUB == 4, "the carried step is the odd step 3 (accumulator Bq)");
+        load_bfrag<D, KT>(tile, 0, lane, bfr);
+        const float tc = tile_mma_epi<D, HB, KT>(qf, bfr, tile, 32, true, CARRY && carry, lane, A, Bq, wv,
+                                                 [&](int kk) { dma(0, kk); });
+        if (CARRY && carry) {                           // the carried tile is complete
+          pv[0] = c_ov0;
+          pv[1] = lane < 32 ? c_tprev : tc;
+          pbase = c_base;
+          carry = false;
+        }
+#pragma unroll
+        for (int s = 1; s < NSUB; ++s) {
+          float tcur;
+          if (s & 1)
+            tcur = tile_mma_epi<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, true, lane, Bq, A, wv,
+                                           [&](int kk) { dma(s, kk); });
+          else
+            tcur = tile_mma_epi<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, true, lane, A, Bq, wv,
+                                           [&](int kk) { dma(s, kk); });
+          if ((s - 1) & 1) ov[(s - 2) / 2] = lane < 32 ? t_prev : tcur;
+          else t_prev = tcur;
+        }
+        if constexpr (CARRY) {
+          carry = true;
+          c_ov0 = ov[0];
+          c_tprev = t_prev;
+          c_base = base;
+        } else {
+          const float tl = tile_epilogue<HB>(Bq, wv);
+          ov[NSUB / 2 - 1] = lane < 32 ? t_prev : tl;
+        }
         if (more) {
           if constexpr (LISTM) {
 #pragma unroll
@@ -553,6 +582,26 @@ score_kernel(ScoreArgs a) {
           if (it + 2 < ntile) fetch_idx(base + 2 * KT);
         }
       }
+    } else if (full) {
+      // full tile (keys staged through registers): the epilogue of each 32-key step overlaps the
+      // MFMAs of the next one
+      float t_prev = 0.f;
+      tile_mma<Mma, D, HB, KT>(qf, tile, 0, lane, A);
+#pragma unroll
+      for (int s = 1; s < NSUB; ++s) {
+        float tcur;
+        if (s & 1) {
+          tile_mma<Mma, D, HB, KT>(qf, tile, s * 32, lane, Bq);
+          tcur = tile_epilogue<HB>(A, wv);
+        } else {
+          tile_mma<Mma, D, HB, KT>(qf, tile, s * 32, lane, A);
+          tcur = tile_epilogue<HB>(Bq, wv);
+        }
+        if ((s - 1) & 1) ov[(s - 2) / 2] = lane < 32 ? t_prev : tcur;
+        else t_prev = tcur;
+      }
+      const float tl = tile_epilogue<HB>(Bq, wv);
+      ov[NSUB / 2 - 1] = lane < 32 ? t_prev : tl;
     } else if (active && base < lim) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
@@ -568,7 +617,7 @@ score_kernel(ScoreArgs a) {
     } else {
       if (more) ld.store(tiles + (cur ^ 1) * G::TILE_BYTES, tid);
     }
-    if (DEFER && full) {
+    if (DEFER && full && !CARRY) {
 #pragma unroll
       for (int p = 0; p < NSUB / 2; ++p) {
         const int n = p * 64 + lane;
@@ -579,8 +628,9 @@ score_kernel(ScoreArgs a) {
         }
       }
       pbase = base;
-    } else if (active) {
-      // partial tile: every LDS access (scale, key list, histogram) before the score stores
+    } else if (active && !(CARRY && full)) {
+      // partial tile (and a key list's full tile): every LDS access (scale, key list, histogram)
+      // before the score stores
       float v[NSUB / 2];
 #pragma unroll
       for (int p = 0; p < NSUB / 2; ++p) {
@@ -604,6 +654,7 @@ score_kernel(ScoreArgs a) {
     lds_barrier();
   }
   flush();
+  finish_carry();
   if (fuse && active) {
     int bin;
     uint32_t above;

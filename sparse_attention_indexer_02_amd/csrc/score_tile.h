@@ -233,20 +233,78 @@ __device__ __forceinline__ void tile_mma_rot(const bf16x8_t (&qf)[HB][Geo<MmaBf1
   }
 }
 
-// ReLU + head-weighted sum of one 32x32 tile per head block; returns the full score of key
-// (lane % 32) in every lane (lanes l and l+32 hold complementary heads; the permlane32 swap
-// exchanges the halves so that both lanes end with the same total).
+// Order of the head-weighted sum: the 16 accumulator registers of each head block are taken in
+// 8 slices of 2 registers; slice by slice, head block by head block, register r goes into partial
+// sum r % 4. Every evaluation of the epilogue (interleaved with MFMAs or not) uses this order, so
+// that a key's score does not depend on the path that computed it.
+constexpr int EPI_SLICES = 8;
+
 template <int HB>
-__device__ __forceinline__ float tile_epilogue(const f32x16_t (&acc)[HB], const float (&wv)[HB][16]) {
-  float p[4] = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void epi_slice(const f32x16_t (&acc)[HB], const float (&wv)[HB][16], int sl,
+                                          float (&p)[4]) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r & 3] = fmaf(wv[hb][r], relu(acc[hb][r]), p[r & 3]);
+    for (int r = 2 * sl; r < 2 * sl + 2; ++r) p[r & 3] = fmaf(wv[hb][r], relu(acc[hb][r]), p[r & 3]);
+}
+
+// Cross-lane finish: lanes l and l+32 hold complementary heads of key l % 32; the permlane32 swap
+// exchanges the halves so that both lanes end with the same total.
+__device__ __forceinline__ float epi_finish(const float (&p)[4]) {
   const float part = (p[0] + p[1]) + (p[2] + p[3]);
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
                                                    false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// ReLU + head-weighted sum of one 32x32 tile per head block; returns the full score of key
+// (lane % 32) in every lane.
+template <int HB>
+__device__ __forceinline__ float tile_epilogue(const f32x16_t (&acc)[HB], const float (&wv)[HB][16]) {
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sl = 0; sl < EPI_SLICES; ++sl) epi_slice<HB>(acc, wv, sl, p);
+  return epi_finish(p);
+}
+
+// One 32-key step of the bf16 path with the previous step's epilogue woven in. Per key fragment
+// kk: the HB MFMAs of this step, the refill of fragment register kk with the next step's
+// fragment from LDS (when `next`), the fragment's share of the previous step's epilogue (when
+// `prev`; slices of epi_slice, in order) and the hook extra(kk) (the next tile's load issue). A
+// scheduling barrier closes each fragment's group, so that the compiler keeps VALU work behind
+// every pair of MFMAs instead of running the MFMAs back to back and the epilogue after them (a
+// wave issues in order: the matrix core is idle while the wave works through a run of VALU
+// instructions). Returns the previous step's scores (when `prev`).
+template <int D, int HB, int KT, class Extra>
+__device__ __forceinline__ float tile_mma_epi(const bf16x8_t (&qf)[HB][Geo<MmaBf16, D, KT>::NKK],
+                                              bf16x8_t (&bf)[Geo<MmaBf16, D, KT>::NKK],
+                                              const uint8_t* tile, int next_n0, bool next, bool prev,
+                                              int lane, f32x16_t (&acc)[HB], const f32x16_t (&pacc)[HB],
+                                              const float (&wv)[HB][16], Extra extra) {
+  typedef Geo<MmaBf16, D, KT> G;
+  constexpr int NKK = G::NKK;
+  static_assert(EPI_SLICES % NKK == 0 || NKK % EPI_SLICES == 0, "epilogue slices per fragment");
+  const int hh = lane >> 5;
+  const int n = next_n0 + (lane & 31);
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+      acc[hb] = MmaBf16::mma(qf[hb][kk], bf[kk], kk == 0 ? f32x16_t{} : acc[hb]);
+    if (next)
+      bf[kk] = *reinterpret_cast<const bf16x8_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + kk));
+    if (prev) {
+#pragma unroll
+      for (int sl = kk * EPI_SLICES / NKK; sl < (kk + 1) * EPI_SLICES / NKK; ++sl) epi_slice<HB>(pacc, wv, sl, p);
+      // the partial sums are materialised here: without this the compiler sinks the whole
+      // epilogue to its single use after the last fragment
+      asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
+    }
+    extra(kk);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return prev ? epi_finish(p) : 0.f;
 }
 
 }  // namespace idx
