@@ -36,9 +36,9 @@ def check_gb(prob, k, G, Bs, keep, gi, gs, gb, groups, name):
         assert (np.diff(kept) > 0).all()
         toks = (kept[:, None] * Bs + np.arange(Bs)[None]).reshape(-1)
         for t in oracle.group_members(prob.T, G, g):
-            d = oracle.dense_row(inp, b, t, k)
-            uni = toks[toks < inp.P(b, t)]
-            check_selection(gi[b, t], gs[b, t], uni, d["all_scores"][uni], d["magnitude"][uni], k,
+            # the oracle's token scores over the GPU's own kept blocks (inside the prefix)
+            r = oracle.refine_row(inp, b, t, k, toks)
+            check_selection(gi[b, t], gs[b, t], r["universe"], r["all_scores"], r["magnitude"], k,
                             prob.D, ctx=f"{name} b{b} t{t}")
 
 
@@ -70,3 +70,18 @@ def test_group_block_keep_all_is_dense():
         r = oracle.dense_row(inp, 0, t, k)
         check_selection(gi[0, t], gs[0, t], r["universe"], r["all_scores"], r["magnitude"], k, p.D,
                         ctx=f"gb-all t{t}", oracle_sel=r["ids"])
+
+
+@pytest.mark.timeout(900)
+def test_gblock128k_full_size_sampled_groups():
+    # the benchmarked shape: 4096 queries at the end of a 131072-token context, groups of 16,
+    # 128-token blocks, 128 kept blocks, so each member refines rows of 16384 list slots
+    spec = W.WORKLOADS["gblock128k"]
+    p = spec["gen"](0)
+    G, Bs, keep, k = spec["group_size"], spec["block_size"], spec["n_blocks_keep"], spec["k"]
+    say("case gblock128k full size (N=131072, 4096 queries, G=16, Bs=128, keep=128, k=2048)")
+    gi, gs, gb = run_gb(p, k, G, Bs, keep)
+    rng = np.random.default_rng(3)
+    groups = sorted(set([0, 1, 128, 255] + list(rng.integers(0, 256, 4))))
+    check_gb(p, k, G, Bs, keep, gi, gs, gb, [(0, g) for g in groups], "gblock128k")
+    assert ((gi[0] >= 0).sum(-1) == k).all()

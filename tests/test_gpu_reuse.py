@@ -25,27 +25,28 @@ def run_reuse(prob, k, G):
     return oi.cpu().numpy(), osc.cpu().numpy()
 
 
-def check_reuse(prob, k, G, gi, gs, name):
+def check_reuse(prob, k, G, gi, gs, name, groups=None):
     inp = oracle.Inputs(prob)
     NG = (prob.T + G - 1) // G
-    for b in range(prob.B):
-        for g in range(NG):
-            mem = list(oracle.group_members(prob.T, G, g))
-            ps = oracle.group_proxy_scan(inp, b, g, G, k)
-            far = max(mem, key=lambda t: prob.q_pos[b, t])
-            check_selection(gi[b, far], gs[b, far], np.arange(ps["P"]), ps["proxy_scores"],
-                            ps["proxy_magnitude"], k, prob.D, ctx=f"{name} b{b} g{g} t{far}",
-                            oracle_sel=ps["cand"])
-            top = gi[b, far][gi[b, far] >= 0]
-            sc = dict(zip(top.tolist(), gs[b, far][gi[b, far] >= 0].view(np.uint32).tolist()))
-            for t in mem:
-                sel = gi[b, t][gi[b, t] >= 0]
-                want = top[top < inp.P(b, t)]
-                assert set(sel.tolist()) == set(want.tolist()), f"{name} b{b} t{t}"
-                assert len(sel) == len(want) and (gi[b, t, len(sel):] == -1).all()
-                got = gs[b, t][: len(sel)].view(np.uint32).tolist()
-                assert got == [sc[v] for v in sel.tolist()], f"{name} b{b} t{t} scores"
-                assert np.isneginf(gs[b, t, len(sel):]).all()
+    if groups is None:
+        groups = [(b, g) for b in range(prob.B) for g in range(NG)]
+    for b, g in groups:
+        mem = list(oracle.group_members(prob.T, G, g))
+        ps = oracle.group_proxy_scan(inp, b, g, G, k)
+        far = max(mem, key=lambda t: prob.q_pos[b, t])
+        check_selection(gi[b, far], gs[b, far], np.arange(ps["P"]), ps["proxy_scores"],
+                        ps["proxy_magnitude"], k, prob.D, ctx=f"{name} b{b} g{g} t{far}",
+                        oracle_sel=ps["cand"])
+        top = gi[b, far][gi[b, far] >= 0]
+        sc = dict(zip(top.tolist(), gs[b, far][gi[b, far] >= 0].view(np.uint32).tolist()))
+        for t in mem:
+            sel = gi[b, t][gi[b, t] >= 0]
+            want = top[top < inp.P(b, t)]
+            assert set(sel.tolist()) == set(want.tolist()), f"{name} b{b} t{t}"
+            assert len(sel) == len(want) and (gi[b, t, len(sel):] == -1).all()
+            got = gs[b, t][: len(sel)].view(np.uint32).tolist()
+            assert got == [sc[v] for v in sel.tolist()], f"{name} b{b} t{t} scores"
+            assert np.isneginf(gs[b, t, len(sel):]).all()
 
 
 def test_reuse_singletons_equal_dense():
@@ -90,3 +91,17 @@ def test_reuse_long_proxy_rows_and_ties():
     check_reuse(p, k, G, gi, gs, "reuse-long")
     far = 3 * G - 1
     assert set(gi[0, far].tolist()) == set(range(k)), "ties: lowest tokens"
+
+
+@pytest.mark.timeout(900)
+def test_reuse64k_full_size_sampled_groups():
+    # the benchmarked shape: L=65536, H=64, D=128, groups of 16, k=2048; the proxies' prefix
+    # scans over up to 65536 keys and the member rows of sampled groups across the prefill
+    spec = W.WORKLOADS["reuse64k"]
+    p = spec["gen"](0)
+    G, k = spec["group_size"], spec["k"]
+    say("case reuse64k full size (L=65536, H=64, D=128, G=16, k=2048)")
+    gi, gs = run_reuse(p, k, G)
+    rng = np.random.default_rng(4)
+    groups = sorted(set([0, 127, 128, 2047, 4095] + list(rng.integers(0, 4096, 4))))
+    check_reuse(p, k, G, gi, gs, "reuse64k", groups=[(0, g) for g in groups])
