@@ -71,12 +71,16 @@ def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
-def queries_f64(q: np.ndarray, q_dtype: int) -> np.ndarray:
+def queries_f64(q: np.ndarray, q_dtype: int, q_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Real query values. FP8 queries carry one fp32 scale per (query, head), the same
+    per-vector quantisation as the FP8 key cache: query = decode(byte) * scale (exact in fp64)."""
     if q_dtype == F32:
         return np.asarray(q, np.float32).astype(np.float64)
     if q_dtype == BF16:
         return bf16_bits_to_f64(q)
-    raise ValueError("query dtype must be F32 or BF16")
+    if q_dtype == FP8_E4M3:
+        return e4m3fn_bits_to_f64(q) * np.asarray(q_scale, np.float32).astype(np.float64)[..., None]
+    raise ValueError("query dtype must be F32, BF16 or FP8_E4M3")
 
 
 def keys_f64(k: np.ndarray, k_dtype: int, k_scale: Optional[np.ndarray]) -> np.ndarray:
@@ -128,7 +132,7 @@ class Inputs:
 
     def __init__(self, prob):
         self.prob = prob
-        self.q = queries_f64(prob.q, prob.q_dtype)        # [B,T,H,D]
+        self.q = queries_f64(prob.q, prob.q_dtype, getattr(prob, "q_scale", None))   # [B,T,H,D]
         self.w = np.asarray(prob.w, np.float32).astype(np.float64)
         self._keys: Dict[int, np.ndarray] = {}
 
@@ -193,6 +197,8 @@ def proxy_query(prob, b: int, g: int, G: int):
 
     Returns (q_bits_or_f32 [H,D], w [H] float32, pos int)."""
     mem = group_members(prob.T, G, g)
+    if prob.q_dtype == FP8_E4M3:
+        raise ValueError("proxy queries are defined for bf16 and fp32 queries")
     if prob.q_dtype == BF16:
         qf = (np.asarray(prob.q[b, mem.start:mem.stop], np.uint16).astype(np.uint32)
               << np.uint32(16)).view(np.float32)

@@ -30,12 +30,14 @@ E4M3_MAX = 448.0
 class Problem:
     """Indexer inputs in storage form (host numpy arrays).
 
-    q      [B,T,H,D]  float32 (q_dtype F32) or uint16 bf16 bit patterns (BF16)
+    q      [B,T,H,D]  float32 (q_dtype F32), uint16 bf16 bit patterns (BF16) or uint8 E4M3FN bits
+                      (FP8_E4M3)
     k      [B,N,D]    float32 (F32), uint16 bf16 bits (BF16) or uint8 E4M3FN bits (FP8_E4M3)
     k_scale[B,N]      float32, only for FP8_E4M3 keys (real key = decoded byte * scale)
     w      [B,T,H]    float32 head weights
     q_pos  [B,T]      int32: key s is visible to query (b,t) iff s <= q_pos[b,t] and s < k_len[b]
     k_len  [B]        int32 valid keys per sequence
+    q_scale[B,T,H]    float32, only for FP8_E4M3 queries (real query = decoded byte * scale)
     """
     q: np.ndarray
     q_dtype: int
@@ -45,6 +47,7 @@ class Problem:
     w: np.ndarray
     q_pos: np.ndarray
     k_len: np.ndarray
+    q_scale: Optional[np.ndarray] = None
 
     @property
     def B(self): return self.q.shape[0]
@@ -138,7 +141,8 @@ def _store(x, dtype):
 
 def make_prefill(L, H, D, *, seed=0, rho=0.9, q_dtype=BF16, k_dtype=BF16, heavy_frac=0.01,
                  heavy_factor=3.0, w_scale=0.125, B=1, iid_queries=False) -> Problem:
-    """One (or B) causal prefill sequence(s): query t sits at position t, k_len = L."""
+    """One (or B) causal prefill sequence(s): query t sits at position t, k_len = L. FP8
+    queries are quantised per (query, head) vector like the FP8 key cache is per token."""
     rng = np.random.default_rng(seed)
     if iid_queries:
         q = rng.standard_normal((B, L, H, D), dtype=np.float32)
@@ -147,11 +151,11 @@ def make_prefill(L, H, D, *, seed=0, rho=0.9, q_dtype=BF16, k_dtype=BF16, heavy_
     keys = rng.standard_normal((B, L, D), dtype=np.float32)
     _heavy_rows(rng, keys, heavy_frac, heavy_factor)
     w = (rng.random((B, L, H), dtype=np.float32) * np.float32(w_scale)).astype(np.float32)
-    qs, _ = _store(q, q_dtype)
+    qs, qsc = _store(q, q_dtype)
     ks, sc = _store(keys, k_dtype)
     q_pos = np.broadcast_to(np.arange(L, dtype=np.int32), (B, L)).copy()
     k_len = np.full(B, L, np.int32)
-    return Problem(qs, q_dtype, ks, k_dtype, sc, w, q_pos, k_len)
+    return Problem(qs, q_dtype, ks, k_dtype, sc, w, q_pos, k_len, q_scale=qsc)
 
 
 def make_tiny(seed=0, L=1024, H=4, D=32, n_heavy=16) -> Problem:
@@ -226,6 +230,12 @@ WORKLOADS = {
                      gen=lambda seed=0: make_prefill(16384, 64, 128, seed=seed, rho=0.9)),
     "dense64k": dict(op="dense", k=2048,
                      gen=lambda seed=0: make_prefill(65536, 64, 128, seed=seed, rho=0.95)),
+    "dense16k_fp8": dict(op="dense", k=2048,
+                         gen=lambda seed=0: make_prefill(16384, 64, 128, seed=seed, rho=0.9,
+                                                         q_dtype=FP8_E4M3, k_dtype=FP8_E4M3)),
+    "dense64k_fp8": dict(op="dense", k=2048,
+                         gen=lambda seed=0: make_prefill(65536, 64, 128, seed=seed, rho=0.95,
+                                                         q_dtype=FP8_E4M3, k_dtype=FP8_E4M3)),
     "decode128k": dict(op="dense", k=2048,
                        gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed)),
     "group64k": dict(op="group", k=2048, group_size=16, n_cand=8192,
