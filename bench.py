@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "indexer query-key pairs/sec + top-k rows/sec at 64K prefill, 128K decode; % roofline"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -314,7 +315,7 @@ class Run:
         self.op = op = spec["op"]
         self.out_idx = torch.empty((B, T, k), dtype=torch.int32, device="cuda:0")
         self.out_sc = torch.empty((B, T, k), dtype=torch.float32, device="cuda:0")
-        p = idx.make_problem(t["q"], t["k"], t["w"], t["q_pos"], t["k_len"], t["k_scale"])
+        p = idx.make_problem(t["q"], t["k"], t["w"], t["q_pos"], t["k_len"], t["k_scale"], t["q_scale"])
         self.banks_np = None
         if op == "dense":
             need = idx.workspace_bytes(idx.OP_SCORE_TOPK, p, k)
@@ -338,7 +339,8 @@ class Run:
         t, k, spec, op = self.t, self.k, self.spec, self.op
         kw = dict(k_len=t["k_len"], out_idx=self.out_idx, out_score=self.out_sc, workspace=self.ws)
         if op == "dense":
-            idx.score_topk(t["q"], t["k"], t["w"], t["q_pos"], topk=k, k_scale=t["k_scale"], **kw)
+            idx.score_topk(t["q"], t["k"], t["w"], t["q_pos"], topk=k, k_scale=t["k_scale"],
+                           q_scale=t["q_scale"], **kw)
         elif op == "group":
             idx.group_proxy_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
                                    group_size=spec["group_size"], n_cand=spec["n_cand"],
@@ -390,11 +392,14 @@ class Run:
             for n, (ms, c) in self.kernels.items() if c))
 
     def _mfma(self, kernel, flops, **extra):
+        import workloads as W
         ms, n = self.kernels["block_refine" if kernel.startswith("block_refine") else "score"]
         per_launch = flops / (n / self.steps)
         achieved = per_launch / (ms / n * 1e-3) / 1e12
-        return {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+        # FP8 queries (with FP8 keys) run on the FP8 matrix cores: their own peak
+        peak = PEAK_FP8_TFLOPS if self.prob.q_dtype == W.FP8_E4M3 else PEAK_BF16_TFLOPS
+        return {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": measured_traffic(self.name, kernel),
                 "per_launch": f"{per_launch:.4g} flop", "mean_launch_ms": ms / n, **extra}
 
@@ -525,7 +530,7 @@ def main():
     out = {"metric": METRIC, "value": main_line["value"], "unit": "pairs/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_line["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16" if q_dtype == W.BF16 else "f32",
+           "dtype": {W.BF16: "bf16", W.FP8_E4M3: "fp8 (e4m3 queries and keys, fp32 accumulate)"}.get(q_dtype, "f32"),
            "data": "synthetic (seeded generators shaped like the pages' workloads)"}
     out.update({k_: v_ for k_, v_ in main_line.items() if k_ not in out})
     if headline:

@@ -41,7 +41,8 @@ extern "C" {
 enum {
   IDX_F32 = 0,       /* IEEE binary32 */
   IDX_BF16 = 1,      /* bfloat16 (upper half of binary32) */
-  IDX_FP8_E4M3 = 2   /* OCP FP8 E4M3FN, one fp32 scale per token: key = decode(byte) * scale */
+  IDX_FP8_E4M3 = 2   /* OCP FP8 E4M3FN with fp32 scales: key = decode(byte) * k_scale[token],
+                        query = decode(byte) * q_scale[query, head] */
 };
 
 /* status codes */
@@ -59,7 +60,8 @@ enum {
 enum { IDX_OP_SCORE_TOPK = 0, IDX_OP_GROUP = 1, IDX_OP_BLOCK = 2, IDX_OP_REFINE = 3, IDX_OP_REUSE = 4 };
 
 /* The indexer's inputs. Layouts are dense and row-major.
- *   q       [B, T, H, D]  q_dtype IDX_F32 or IDX_BF16
+ *   q       [B, T, H, D]  q_dtype IDX_F32, IDX_BF16, or IDX_FP8_E4M3 (dense entry points only,
+ *                         with FP8 keys and D in {64, 128}: both operands on the FP8 matrix cores)
  *   k       [B, N, D]     k_dtype IDX_F32, IDX_BF16 or IDX_FP8_E4M3 (the per-layer key cache)
  *   k_scale [B, N] fp32   required iff k_dtype == IDX_FP8_E4M3, else ignored
  *   w       [B, T, H] fp32 head weights, any sign
@@ -67,6 +69,8 @@ enum { IDX_OP_SCORE_TOPK = 0, IDX_OP_GROUP = 1, IDX_OP_BLOCK = 2, IDX_OP_REFINE 
  *                         s <= q_pos[b,t] and s < k_len[b] (the query's own token is visible);
  *                         q_pos < 0 means an empty prefix
  *   k_len   [B] int32     keys present in each sequence's cache, or NULL for N
+ *   q_scale [B, T, H] fp32 required iff q_dtype == IDX_FP8_E4M3, else ignored; scales >= 0 and
+ *                         finite (a precondition, like k_scale)
  * Built shapes: H in 1..128, D in {32, 64, 128}. Prefill (T large) and decode (T = 1..4 multi-token
  * prediction queries against a long cache) use the same call; decode-shaped problems (bf16
  * queries, FP8 or bf16 keys, H <= 64, D in {64, 128}, T <= 4, N >= 2048) take a streaming path
@@ -80,13 +84,20 @@ typedef struct idx_problem {
   const float* w;
   const int32_t* q_pos;
   const int32_t* k_len;
+  const float* q_scale;
 } idx_problem;
 
 /* Dense lightning indexer: score every visible key of every query and keep the top k.
  *   out_idx   [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional).
+ * FP8 queries with FP8 keys run the q.k contraction on FP8 x FP8 matrix cores: the dot product
+ * of the stored bytes is accumulated in fp32, then each head's weight times its query scale and
+ * the key's scale are applied (both scales >= 0 factor out of the ReLU). The other entry points
+ * take F32 or BF16 queries (IDX_ERR_UNSUPPORTED for FP8 queries).
  * Source: the indexer itself ("Multi-layer Indexer ...", authors' abstract: every layer's indexer
  * scores the whole cache and keeps the k = 2048 best tokens; "PIVOT ...", abstract: the scan over
- * every preceding token costs O(L^2) per layer). */
+ * every preceding token costs O(L^2) per layer); its scoring on FP8 matrix cores follows the
+ * LatentIndex page's ("LatentIndex: Cross-Layer Sharing ...", abstract) aim of a cheaper indexer
+ * scan. */
 int idx_score_topk(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
                    void* ws, size_t ws_bytes, void* stream);
 

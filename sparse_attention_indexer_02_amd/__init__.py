@@ -13,7 +13,8 @@ error (there is no other implementation to fall back to).
     idx, score, blocks = group_block_refine(q, k, w, q_pos, topk=2048, group_size=16,
                                             block_size=128, n_blocks_keep=128)
 
-Shapes: q [B,T,H,D] (bf16 or fp32), k [B,N,D] (bf16, fp32, or float8_e4m3fn / uint8 E4M3FN
+Shapes: q [B,T,H,D] (bf16 or fp32; float8_e4m3fn / uint8 E4M3FN bytes with q_scale [B,T,H] fp32
+for score_topk), k [B,N,D] (bf16, fp32, or float8_e4m3fn / uint8 E4M3FN
 bytes with k_scale [B,N] fp32), w [B,T,H] fp32, q_pos [B,T] int32, k_len [B] int32 or None.
 Outputs: int32 [B,T,topk] token-index sets (order within a row unspecified, -1 padded) and the
 matching fp32 scores (-inf padded).
@@ -47,7 +48,7 @@ class Problem(ctypes.Structure):
                 ("D", ctypes.c_int32), ("N", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("k_dtype", ctypes.c_int32), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("w", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
-                ("k_len", ctypes.c_void_p)]
+                ("k_len", ctypes.c_void_p), ("q_scale", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -107,6 +108,8 @@ def _qcode(t):
         return BF16
     if t.dtype == torch.float32:
         return F32
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FP8_E4M3
     raise IdxError(f"unsupported query dtype {t.dtype}")
 
 
@@ -120,8 +123,9 @@ def _kcode(t):
     raise IdxError(f"unsupported key dtype {t.dtype}")
 
 
-def make_problem(q, k, w, q_pos, k_len=None, k_scale=None) -> Problem:
-    """Fill the ABI's problem struct from tensors (shape checks only)."""
+def make_problem(q, k, w, q_pos, k_len=None, k_scale=None, q_scale=None) -> Problem:
+    """Fill the ABI's problem struct from tensors (shape checks only). FP8 queries (float8_e4m3fn
+    or uint8 E4M3FN bytes) need q_scale float32 [B,T,H]."""
     if q.dim() != 4 or k.dim() != 3 or w.dim() != 3 or q_pos.dim() != 2:
         raise IdxError("expected q [B,T,H,D], k [B,N,D], w [B,T,H], q_pos [B,T]")
     B, T, H, D = q.shape
@@ -137,8 +141,13 @@ def make_problem(q, k, w, q_pos, k_len=None, k_scale=None) -> Problem:
     if kc == FP8_E4M3 and (k_scale is None or k_scale.dtype != torch.float32 or
                            tuple(k_scale.shape) != (B, N)):
         raise IdxError("fp8 keys need k_scale float32 [B,N]")
-    return Problem(B, T, H, D, N, _qcode(q), kc, _ptr(q), _ptr(k),
-                   _ptr(k_scale) if kc == FP8_E4M3 else None, _ptr(w), _ptr(q_pos), _ptr(k_len))
+    qc = _qcode(q)
+    if qc == FP8_E4M3 and (q_scale is None or q_scale.dtype != torch.float32 or
+                           tuple(q_scale.shape) != (B, T, H)):
+        raise IdxError("fp8 queries need q_scale float32 [B,T,H]")
+    return Problem(B, T, H, D, N, qc, kc, _ptr(q), _ptr(k),
+                   _ptr(k_scale) if kc == FP8_E4M3 else None, _ptr(w), _ptr(q_pos), _ptr(k_len),
+                   _ptr(q_scale) if qc == FP8_E4M3 else None)
 
 
 def workspace_bytes(op: int, p: Problem, topk: int, p1: int = 0, p2: int = 0) -> int:
@@ -169,9 +178,9 @@ def _workspace(q, need, workspace):
 
 
 def score_topk(q, k, w, q_pos, topk: int = 2048, k_len=None, k_scale=None, out_idx=None,
-               out_score=None, want_score: bool = True, workspace=None, stream=None):
+               out_score=None, want_score: bool = True, workspace=None, stream=None, q_scale=None):
     """Dense lightning indexer (idx_score_topk)."""
-    p = make_problem(q, k, w, q_pos, k_len, k_scale)
+    p = make_problem(q, k, w, q_pos, k_len, k_scale, q_scale)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     need = workspace_bytes(OP_SCORE_TOPK, p, topk)
     ws = _workspace(q, need, workspace)
@@ -182,10 +191,10 @@ def score_topk(q, k, w, q_pos, topk: int = 2048, k_len=None, k_scale=None, out_i
 
 
 def score_topk_noalloc(q, k, w, q_pos, topk: int = 2048, k_len=None, k_scale=None, out_idx=None,
-                       out_score=None, stream=None):
+                       out_score=None, stream=None, q_scale=None):
     """Dense lightning indexer on the library's static scratch (idx_score_topk_noalloc): the
     outputs must be passed in for an allocation-free call."""
-    p = make_problem(q, k, w, q_pos, k_len, k_scale)
+    p = make_problem(q, k, w, q_pos, k_len, k_scale, q_scale)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, True)
     _check(lib().idx_score_topk_noalloc(ctypes.byref(p), topk, _ptr(out_idx), _ptr(out_score),
                                         _stream(q, stream)),

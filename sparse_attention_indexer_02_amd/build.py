@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libidx.so")
-SOURCES = ["abi.hip", "score.hip", "score_bb128.hip", "score_bb64.hip", "score_bb32_b8.hip",
+SOURCES = ["abi.hip", "score.hip", "score_f8f8.hip", "score_bb128.hip", "score_bb64.hip", "score_bb32_b8.hip",
            "score_f32_f32_d128.hip", "score_f32_bf16_d128.hip", "score_f32_fp8_d128.hip",
            "score_f32_f32_d32_64.hip", "score_f32_bf16_d32_64.hip", "score_f32_fp8_d32_64.hip",
            "block_refine.hip", "decode.hip", "topk.hip", "prep.hip"]

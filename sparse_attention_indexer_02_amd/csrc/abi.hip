@@ -72,7 +72,9 @@ int validate(const idx_problem* p, int32_t k, const int32_t* out_idx, const floa
   if (p->B <= 0 || p->T <= 0 || p->H <= 0 || p->D <= 0 || p->N <= 0 || k <= 0)
     return IDX_ERR_INVALID_ARG;
   if (!p->q || !p->k || !p->w || !p->q_pos || !out_idx) return IDX_ERR_INVALID_ARG;
-  if (p->q_dtype != IDX_F32 && p->q_dtype != IDX_BF16) return IDX_ERR_UNSUPPORTED;
+  if (p->q_dtype != IDX_F32 && p->q_dtype != IDX_BF16 && p->q_dtype != IDX_FP8_E4M3)
+    return IDX_ERR_UNSUPPORTED;
+  if (p->q_dtype == IDX_FP8_E4M3 && !p->q_scale) return IDX_ERR_INVALID_ARG;
   if (p->k_dtype != IDX_F32 && p->k_dtype != IDX_BF16 && p->k_dtype != IDX_FP8_E4M3)
     return IDX_ERR_UNSUPPORTED;
   if (p->k_dtype == IDX_FP8_E4M3 && !p->k_scale) return IDX_ERR_INVALID_ARG;
@@ -81,6 +83,7 @@ int validate(const idx_problem* p, int32_t k, const int32_t* out_idx, const floa
     return IDX_ERR_UNSUPPORTED;
   if (!aligned(p->q, 16) || !aligned(p->k, 16) || !aligned(p->w, 4) || !aligned(p->q_pos, 4) ||
       (p->k_len && !aligned(p->k_len, 4)) || (p->k_scale && !aligned(p->k_scale, 4)) ||
+      (p->q_dtype == IDX_FP8_E4M3 && !aligned(p->q_scale, 4)) ||
       !aligned(out_idx, 4) || (out_score && !aligned(out_score, 4)))
     return IDX_ERR_ALIGN;
   return IDX_OK;
@@ -316,6 +319,7 @@ ScoreArgs base_score_args(const idx_problem* p) {
   ScoreArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = p->q; a.q_dtype = p->q_dtype; a.w = p->w; a.q_pos = p->q_pos;
+  a.q_scale = p->q_dtype == IDX_FP8_E4M3 ? p->q_scale : nullptr;
   a.keys = p->k; a.k_dtype = p->k_dtype; a.k_scale = p->k_scale; a.k_len = p->k_len;
   a.B = p->B; a.T = p->T; a.H = p->H; a.D = p->D;
   a.key_cap = p->N; a.tok_cap = p->N;
@@ -400,7 +404,9 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
     a.scores = pl.scores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
     // bf16 rows of up to 65536 slots: each score-kernel wave selects its own row
-    const bool self_select = p->q_dtype == IDX_BF16 && p->k_dtype == IDX_BF16 && p->N <= 65536;
+    const bool self_select = ((p->q_dtype == IDX_BF16 && p->k_dtype == IDX_BF16) ||
+                              (p->q_dtype == IDX_FP8_E4M3 && p->k_dtype == IDX_FP8_E4M3)) &&
+                             p->N <= 65536;
     if (self_select) {
       a.sel_idx = out_idx; a.sel_score = out_score; a.sel_T = p->T;
     }
@@ -452,6 +458,7 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
                float* out_score, int32_t* out_cand, void* ws, size_t ws_bytes, hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
+  if (p->q_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;     // FP8 queries: dense entry points only
   if (G < 1 || C < 1) return IDX_ERR_INVALID_ARG;
   if (out_cand && !aligned(out_cand, 4)) return IDX_ERR_ALIGN;
   GroupPlan pl = plan_group(p, G, C, nullptr, out_cand);
@@ -517,6 +524,7 @@ int reuse_impl(const idx_problem* p, int32_t k, int32_t G, int32_t* out_idx, flo
                void* ws, size_t ws_bytes, hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
+  if (p->q_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;     // FP8 queries: dense entry points only
   if (G < 1) return IDX_ERR_INVALID_ARG;
   ReusePlan pl = plan_reuse(p, G, k, nullptr);
   if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
@@ -586,6 +594,7 @@ int group_block_impl(const idx_problem* p, int32_t k, int32_t G, int32_t Bs, int
                      hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
+  if (p->q_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;     // FP8 queries: dense entry points only
   if (G < 1 || Bs < 1 || keep < 1) return IDX_ERR_INVALID_ARG;
   if (p->k_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;
   if ((p->N + (int64_t)Bs - 1) / Bs > 65536 || keep > 32767) return IDX_ERR_UNSUPPORTED;
@@ -658,6 +667,7 @@ int refine_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, const int
                 hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
+  if (p->q_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;     // FP8 queries: dense entry points only
   if (G < 1 || C < 1 || !cand) return IDX_ERR_INVALID_ARG;
   if (!aligned(cand, 4) || (cand_cnt && !aligned(cand_cnt, 4))) return IDX_ERR_ALIGN;
   if (p->N > 32768 * 32) return IDX_ERR_UNSUPPORTED;  // the set is built in an LDS bitmap of N bits
@@ -677,6 +687,7 @@ int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_
                float* out_score, int32_t* out_blocks, void* ws, size_t ws_bytes, hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
+  if (p->q_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;     // FP8 queries: dense entry points only
   if (Bs < 1 || keep < 1) return IDX_ERR_INVALID_ARG;
   if (p->k_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;
   if ((p->N + (int64_t)Bs - 1) / Bs > 65536 || keep > 32767) return IDX_ERR_UNSUPPORTED;

@@ -192,7 +192,7 @@ block_refine_direct_kernel(BlockRefineArgs a) {
   constexpr int KT = 128;
   constexpr int NSUB = KT / 32;
   typedef Geo<MmaBf16, D, KT> G;
-  typedef DirectLoader<D, NTHR, KT> DLoader;
+  typedef DirectLoader<MmaBf16, D, NTHR, KT> DLoader;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tiles = smem;
   int16_t* pos_tab = reinterpret_cast<int16_t*>(smem + 2 * G::TILE_BYTES);   // [NW][UMAX]
@@ -349,7 +349,7 @@ block_refine_direct_kernel(BlockRefineArgs a) {
       };
       if (own == (1u << NSUB) - 1u) {
         f32x16_t A[HB], Bq[HB];
-        load_bfrag<D, KT>(tile, 0, lane, bfr);
+        load_bfrag<MmaBf16, D, KT>(tile, 0, lane, bfr);
         tile_mma_rot<D, HB, KT>(qf, bfr, tile, 32, true, lane, A);
 #pragma unroll
         for (int s = 1; s < NSUB; ++s) {
@@ -374,7 +374,7 @@ block_refine_direct_kernel(BlockRefineArgs a) {
         for (int s = 0; s < NSUB; ++s) {
           if (own & (1u << s)) {
             f32x16_t acc[HB];
-            load_bfrag<D, KT>(tile, s * 32, lane, bfr);
+            load_bfrag<MmaBf16, D, KT>(tile, s * 32, lane, bfr);
             tile_mma_rot<D, HB, KT>(qf, bfr, tile, 0, false, lane, acc);
             put(s, tile_epilogue<HB>(acc, wv));
           }

@@ -24,6 +24,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
 // ---------------------------------------------------------------------------------------------
 // number formats
@@ -90,6 +91,17 @@ struct MmaBf16 {
   }
 };
 
+// FP8 x FP8 (OCP E4M3FN both): 32x32x64 with fp32 accumulation, 32 elements (bytes) per lane
+// per operand; the block scales of the instruction are 1 (E8M0 127).
+struct MmaFp8 {
+  static constexpr int kElemBytes = 1;
+  static constexpr int E = 32;
+  typedef i32x8_t frag_t;
+  static __device__ __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
 struct MmaF32 {
   static constexpr int kElemBytes = 4;
   static constexpr int E = 1;
@@ -115,6 +127,14 @@ __device__ __forceinline__ bf16x8_t load_frag<MmaBf16>(const void* row, int dtyp
   // only bf16 storage reaches here (queries of the bf16 path)
   u32x4_t v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(row) + e0);
   return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <>
+__device__ __forceinline__ i32x8_t load_frag<MmaFp8>(const void* row, int dtype, int e0) {
+  // only E4M3 bytes reach here (queries of the FP8 path)
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(row) + e0);
+  const u32x4_t lo = src[0], hi = src[1];
+  return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
 template <>

@@ -17,6 +17,7 @@ enum { MODE_RANGE = 0, MODE_LIST = 1 };
 
 struct ScoreArgs {
   const void* q; int q_dtype;      // [B, T, H, D]
+  const float* q_scale;            // [B, T, H] (FP8 queries) or null
   const float* w;                  // [B, T, H]
   const int32_t* q_pos;            // [B, T]
   const void* keys; int k_dtype;   // [B, key_cap, D]

@@ -13,12 +13,17 @@
 // build). FP8 keys carry one fp32 scale per token; because the scale is positive it factors out
 // of the ReLU and the head sum, so it is applied once per key after the reduction.
 #pragma once
+#include <type_traits>
+
 #include "score_tile.h"
 
 namespace idx {
 
+// Keys already in the MFMA element format stream straight into LDS: bf16 keys for the bf16 MFMA,
+// FP8 keys for the FP8 MFMA.
 template <class Mma, int KST> struct Direct {
-  static constexpr bool value = sizeof(Mma) > 0 && Mma::E == 8 && KST == DT_BF16;
+  static constexpr bool value = (std::is_same<Mma, MmaBf16>::value && KST == DT_BF16) ||
+                                (std::is_same<Mma, MmaFp8>::value && KST == DT_FP8);
 };
 template <class Mma, int KST> struct TileKeys {
   static constexpr int value = Direct<Mma, KST>::value ? 128 : 64;
@@ -263,7 +268,7 @@ score_kernel(ScoreArgs a) {
   static_assert(!Direct<Mma, KST>::value || NSUB >= 2, "direct tiles span several 32-key steps");
   typedef Geo<Mma, D, KT> G;
   typedef TileLoader<Mma, D, KST, NTHR, KT> Loader;
-  typedef DirectLoader<D, NTHR, KT> DLoader;
+  typedef DirectLoader<Mma, D, NTHR, KT> DLoader;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tiles = smem;
   int32_t* skey = reinterpret_cast<int32_t*>(smem + 2 * G::TILE_BYTES);   // [2][KT]
@@ -387,6 +392,13 @@ score_kernel(ScoreArgs a) {
           wv[hb][r] = (active && h < a.H) ? wrow[h] : 0.f;
         }
       }
+      // FP8 queries: each head's query scale is a factor of that head's weight (both >= 0 under
+      // ReLU: w ReLU(c x) = (w c) ReLU(x))
+      if constexpr (std::is_same<Mma, MmaFp8>::value) {
+        const float* qsrow = a.q_scale + ((int64_t)b * a.T + (active ? t : 0)) * a.H;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wv[hb][r] *= qsrow[min(acc_head(hb, r, lane), a.H - 1)];
+      }
     }
   }
 
@@ -450,7 +462,7 @@ score_kernel(ScoreArgs a) {
   __syncthreads();
 
   float* srow = a.scores + ((int64_t)b * a.rows_per_seq + (active ? t - row0 : 0)) * a.score_stride;
-  bf16x8_t bfr[DIRECT ? G::NKK : 1];                 // rotating key fragments (bf16 path)
+  typename Mma::frag_t bfr[DIRECT ? G::NKK : 1];     // rotating key fragments (direct paths)
 
   // Scores of a full tile are counted and stored at the start of the next tile, before its
   // first load: the compiler waits for every outstanding vector memory operation before an LDS
@@ -489,12 +501,17 @@ score_kernel(ScoreArgs a) {
   f32x16_t A[HB], Bq[HB];                             // step accumulators (Bq: the carried step)
   bool carry = false;
   float c_ov0 = 0.f, c_tprev = 0.f;                   // the carried tile's other scores
+  float c_ks[NSUB / 2] = {};                          // and its FP8 key scales
   int c_base = 0;
   auto finish_carry = [&]() {                         // carried step's epilogue without MFMAs
     if (CARRY && carry) {
       const float tl = tile_epilogue<HB>(Bq, wv);
       pv[0] = c_ov0;
       pv[1] = lane < 32 ? c_tprev : tl;
+      if constexpr (KST == DT_FP8) {
+        pv[0] *= c_ks[0];
+        pv[1] *= c_ks[1];
+      }
       pbase = c_base;
       carry = false;
       flush();
@@ -519,6 +536,29 @@ score_kernel(ScoreArgs a) {
       }
     }
     const uint8_t* tile = tiles + cur * G::TILE_BYTES;
+    // FP8 keys: the per-token scale multiplies a key's reduced score. Direct key ranges load the
+    // scales of this tile's slots into registers here, used once the tile's scores are done;
+    // staged tiles keep them in LDS next to the key indices
+    float ksc[NSUB / 2];
+#pragma unroll
+    for (int p = 0; p < NSUB / 2; ++p) ksc[p] = 1.f;
+    if constexpr (DIRECT && KST == DT_FP8 && !LISTM) {
+#pragma unroll
+      for (int p = 0; p < NSUB / 2; ++p)
+        ksc[p] = a.k_scale[(int64_t)b * a.key_cap + min(base + p * 64 + lane, a.key_cap - 1)];
+    }
+    auto tile_scale = [&](int p) -> float {           // scale of slot base + 64 p + lane
+      if constexpr (KST != DT_FP8) {
+        return 1.f;
+      } else if constexpr (!DIRECT) {
+        return sscale[cur * KT + p * 64 + lane];
+      } else if constexpr (LISTM) {
+        const int ki = skey[cur * KT + p * 64 + lane];
+        return ki >= 0 ? a.k_scale[(int64_t)b * a.key_cap + ki] : 0.f;
+      } else {
+        return ksc[p];
+      }
+    };
     // scores of this tile, two 32-key steps per value (lanes 0-31: even step, 32-63: odd step)
     float ov[NSUB / 2];
 #pragma unroll
@@ -531,23 +571,30 @@ score_kernel(ScoreArgs a) {
       // idle buffer with rows already read (no branch inside the MFMA stream)
       float t_prev = 0.f;
       constexpr int IT = DIRECT ? DLoader::ITERS : 1;
+      // (the j-th chunk of a step goes out at fragment 2 j + 1, or at the step's last fragment
+      // when the step has fewer fragments: every chunk is issued in every case)
       auto dma = [&](int s, int kk) {
         if constexpr (DIRECT) {
           const int i0 = (s * IT + NSUB - 2) / (NSUB - 1);
           const int i1 = min(IT, ((s + 1) * IT + NSUB - 2) / (NSUB - 1));
-          const int i = i0 + (kk - 1) / 2;
-          if ((kk & 1) && i < i1)
-            DLoader::load_chunk(i, kseq, tiles + (cur ^ 1) * G::TILE_BYTES, wave, lane, chunk_key(base + KT, i));
+#pragma unroll
+          for (int i = i0; i < i1; ++i)
+            if (min(2 * (i - i0) + 1, G::NKK - 1) == kk)
+              DLoader::load_chunk(i, kseq, tiles + (cur ^ 1) * G::TILE_BYTES, wave, lane, chunk_key(base + KT, i));
         }
       };
       if constexpr (DIRECT) {
         static_assert(NSUB == 4, "the carried step is the odd step 3 (accumulator Bq)");
-        load_bfrag<D, KT>(tile, 0, lane, bfr);
-        const float tc = tile_mma_epi<D, HB, KT>(qf, bfr, tile, 32, true, CARRY && carry, lane, A, Bq, wv,
+        load_bfrag<Mma, D, KT>(tile, 0, lane, bfr);
+        const float tc = tile_mma_epi<Mma, D, HB, KT>(qf, bfr, tile, 32, true, CARRY && carry, lane, A, Bq, wv,
                                                  [&](int kk) { dma(0, kk); });
         if (CARRY && carry) {                           // the carried tile is complete
           pv[0] = c_ov0;
           pv[1] = lane < 32 ? c_tprev : tc;
+          if constexpr (KST == DT_FP8) {
+            pv[0] *= c_ks[0];
+            pv[1] *= c_ks[1];
+          }
           pbase = c_base;
           carry = false;
         }
@@ -555,10 +602,10 @@ score_kernel(ScoreArgs a) {
         for (int s = 1; s < NSUB; ++s) {
           float tcur;
           if (s & 1)
-            tcur = tile_mma_epi<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, true, lane, Bq, A, wv,
+            tcur = tile_mma_epi<Mma, D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, true, lane, Bq, A, wv,
                                            [&](int kk) { dma(s, kk); });
           else
-            tcur = tile_mma_epi<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, true, lane, A, Bq, wv,
+            tcur = tile_mma_epi<Mma, D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, true, lane, A, Bq, wv,
                                            [&](int kk) { dma(s, kk); });
           if ((s - 1) & 1) ov[(s - 2) / 2] = lane < 32 ? t_prev : tcur;
           else t_prev = tcur;
@@ -568,6 +615,8 @@ score_kernel(ScoreArgs a) {
           c_ov0 = ov[0];
           c_tprev = t_prev;
           c_base = base;
+#pragma unroll
+          for (int p = 0; p < NSUB / 2; ++p) c_ks[p] = ksc[p];
         } else {
           const float tl = tile_epilogue<HB>(Bq, wv);
           ov[NSUB / 2 - 1] = lane < 32 ? t_prev : tl;
@@ -622,7 +671,7 @@ score_kernel(ScoreArgs a) {
       for (int p = 0; p < NSUB / 2; ++p) {
         const int n = p * 64 + lane;
         pv[p] = ov[p];
-        if constexpr (KST == DT_FP8) pv[p] *= sscale[cur * KT + n];
+        if constexpr (KST == DT_FP8) pv[p] *= tile_scale(p);
         if constexpr (LISTM) {
           if (skey[cur * KT + n] > my_pos) pv[p] = -INFINITY;
         }
@@ -637,7 +686,7 @@ score_kernel(ScoreArgs a) {
         const int n = p * 64 + lane;
         v[p] = ov[p];
         if (base + n < lim) {
-          if constexpr (KST == DT_FP8) v[p] *= sscale[cur * KT + n];
+          if constexpr (KST == DT_FP8) v[p] *= tile_scale(p);
           if constexpr (LISTM) {
             if (skey[cur * KT + n] > my_pos) v[p] = -INFINITY;
           }

@@ -12,8 +12,13 @@ struct Geo {
   static constexpr int CPR = ROW_BYTES / 16;          // 16-byte chunks per key row
   static constexpr int EPC = 16 / EB;                 // elements per chunk
   static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+  // rows shorter than the 256-byte bank cycle: consecutive rows share it, so the XOR key is the
+  // row index with those rows folded together (then 16 rows read by one phase of a 16-byte
+  // read land in 16 distinct 16-byte bank groups)
+  static constexpr int SWZ_SH = ROW_BYTES >= 256 ? 0 : (ROW_BYTES == 128 ? 1 : 2);
   static constexpr int TILE_BYTES = KT * ROW_BYTES;
   static constexpr int NKK = D / 2 / Mma::E;          // MFMA steps per 32x32 tile
+  static constexpr int CPF = Mma::E * EB / 16;        // 16-byte chunks per lane per fragment
 };
 
 template <int HB> struct WavesFor { static constexpr int value = (HB <= 2) ? 8 : 4; };
@@ -21,8 +26,11 @@ template <int HB> struct WavesFor { static constexpr int value = (HB <= 2) ? 8 :
 // Byte offset inside a tile of logical 16-byte chunk c of key row n (XOR swizzle: the 32 rows a
 // wave reads in one step start in different banks).
 template <class G>
+__device__ __forceinline__ int swz(int n) { return (n >> G::SWZ_SH) & G::SWZ; }
+
+template <class G>
 __device__ __forceinline__ int chunk_off(int n, int c) {
-  return n * G::ROW_BYTES + ((c ^ (n & G::SWZ)) << 4);
+  return n * G::ROW_BYTES + ((c ^ swz<G>(n)) << 4);
 }
 
 // Stages one tile of KT keys from global memory (any key storage format) into LDS in the MFMA
@@ -109,9 +117,9 @@ struct TileLoader {
 // writing bytes [16 i, 16 i + 16); the lane therefore fetches the global chunk that the
 // swizzled layout puts at that position. Invalid keys fetch key row 0 of the sequence (finite
 // data whose scores are never stored). Completion: s_waitcnt vmcnt(0) before the barrier.
-template <int D, int NTHR, int KT>
+template <class Mma, int D, int NTHR, int KT>
 struct DirectLoader {
-  typedef Geo<MmaBf16, D, KT> G;
+  typedef Geo<Mma, D, KT> G;
   static constexpr int NCH = KT * G::CPR;
   static constexpr int NWAVE = NTHR / 64;
   static constexpr int ITERS = NCH / NTHR > 0 ? NCH / NTHR : 1;
@@ -135,7 +143,7 @@ struct DirectLoader {
     const int blk = i * NWAVE + wave;                // 1 KB LDS block written by this instr
     const int p = blk * 64 + lane;
     const int n = p / G::CPR, cp = p % G::CPR;
-    const int c = cp ^ (n & G::SWZ);                 // logical chunk stored at p
+    const int c = cp ^ swz<G>(n);                    // logical chunk stored at p
     const uint8_t* src = kseq + (int64_t)(ki >= 0 ? ki : 0) * G::ROW_BYTES + c * 16;
     __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
                                               reinterpret_cast<uintptr_t>(tile + blk * 1024)),
@@ -167,6 +175,22 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// B fragment kk of key row n for lane half hh (direct paths): CPF consecutive logical chunks,
+// starting at chunk CPF (hh NKK + kk); queries are loaded with the same element order.
+template <class Mma, class G>
+__device__ __forceinline__ typename Mma::frag_t read_frag(const uint8_t* tile, int n, int hh, int kk) {
+  if constexpr (G::CPF == 1) {
+    return *reinterpret_cast<const typename Mma::frag_t*>(tile + chunk_off<G>(n, hh * G::NKK + kk));
+  } else {
+    static_assert(G::CPF == 2, "one or two 16-byte chunks per fragment");
+    const int c = 2 * (hh * G::NKK + kk);
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(tile + chunk_off<G>(n, c));
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(tile + chunk_off<G>(n, c + 1));
+    return typename Mma::frag_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+}
+
 // One wave: x = q(32*HB heads) . k(32 keys of the tile starting at row n0) accumulated in acc.
 template <class Mma, int D, int HB, int KT>
 __device__ __forceinline__ void tile_mma(const typename Mma::frag_t (&qf)[HB][Geo<Mma, D, KT>::NKK],
@@ -175,11 +199,10 @@ __device__ __forceinline__ void tile_mma(const typename Mma::frag_t (&qf)[HB][Ge
   typedef Geo<Mma, D, KT> G;
   const int hh = lane >> 5;
   const int n = n0 + (lane & 31);
-  if constexpr (Mma::E == 8) {
-    bf16x8_t bf[G::NKK];
+  if constexpr (Mma::E > 1) {
+    typename Mma::frag_t bf[G::NKK];
 #pragma unroll
-    for (int kk = 0; kk < G::NKK; ++kk)
-      bf[kk] = *reinterpret_cast<const bf16x8_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + kk));
+    for (int kk = 0; kk < G::NKK; ++kk) bf[kk] = read_frag<Mma, G>(tile, n, hh, kk);
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) acc[hb] = Mma::mma(qf[hb][0], bf[0], f32x16_t{});
 #pragma unroll
@@ -200,16 +223,15 @@ __device__ __forceinline__ void tile_mma(const typename Mma::frag_t (&qf)[HB][Ge
   }
 }
 
-// B fragments (the 32 keys' halves of the head dimension) of one 32-key step, bf16 path.
-template <int D, int KT>
+// B fragments (the 32 keys' halves of the head dimension) of one 32-key step, direct paths.
+template <class Mma, int D, int KT>
 __device__ __forceinline__ void load_bfrag(const uint8_t* tile, int n0, int lane,
-                                           bf16x8_t (&bf)[Geo<MmaBf16, D, KT>::NKK]) {
-  typedef Geo<MmaBf16, D, KT> G;
+                                           typename Mma::frag_t (&bf)[Geo<Mma, D, KT>::NKK]) {
+  typedef Geo<Mma, D, KT> G;
   const int hh = lane >> 5;
   const int n = n0 + (lane & 31);
 #pragma unroll
-  for (int kk = 0; kk < G::NKK; ++kk)
-    bf[kk] = *reinterpret_cast<const bf16x8_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + kk));
+  for (int kk = 0; kk < G::NKK; ++kk) bf[kk] = read_frag<Mma, G>(tile, n, hh, kk);
 }
 
 // bf16 path: MFMAs of one 32-key step from fragments already in registers; when `next` is
@@ -228,8 +250,7 @@ __device__ __forceinline__ void tile_mma_rot(const bf16x8_t (&qf)[HB][Geo<MmaBf1
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
       acc[hb] = MmaBf16::mma(qf[hb][kk], bf[kk], kk == 0 ? f32x16_t{} : acc[hb]);
-    if (next)
-      bf[kk] = *reinterpret_cast<const bf16x8_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + kk));
+    if (next) bf[kk] = read_frag<MmaBf16, G>(tile, n, hh, kk);
   }
 }
 
@@ -275,13 +296,13 @@ __device__ __forceinline__ float tile_epilogue(const f32x16_t (&acc)[HB], const 
 // every pair of MFMAs instead of running the MFMAs back to back and the epilogue after them (a
 // wave issues in order: the matrix core is idle while the wave works through a run of VALU
 // instructions). Returns the previous step's scores (when `prev`).
-template <int D, int HB, int KT, class Extra>
-__device__ __forceinline__ float tile_mma_epi(const bf16x8_t (&qf)[HB][Geo<MmaBf16, D, KT>::NKK],
-                                              bf16x8_t (&bf)[Geo<MmaBf16, D, KT>::NKK],
+template <class Mma, int D, int HB, int KT, class Extra>
+__device__ __forceinline__ float tile_mma_epi(const typename Mma::frag_t (&qf)[HB][Geo<Mma, D, KT>::NKK],
+                                              typename Mma::frag_t (&bf)[Geo<Mma, D, KT>::NKK],
                                               const uint8_t* tile, int next_n0, bool next, bool prev,
                                               int lane, f32x16_t (&acc)[HB], const f32x16_t (&pacc)[HB],
                                               const float (&wv)[HB][16], Extra extra) {
-  typedef Geo<MmaBf16, D, KT> G;
+  typedef Geo<Mma, D, KT> G;
   constexpr int NKK = G::NKK;
   static_assert(EPI_SLICES % NKK == 0 || NKK % EPI_SLICES == 0, "epilogue slices per fragment");
   const int hh = lane >> 5;
@@ -291,9 +312,8 @@ __device__ __forceinline__ float tile_mma_epi(const bf16x8_t (&qf)[HB][Geo<MmaBf
   for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
-      acc[hb] = MmaBf16::mma(qf[hb][kk], bf[kk], kk == 0 ? f32x16_t{} : acc[hb]);
-    if (next)
-      bf[kk] = *reinterpret_cast<const bf16x8_t*>(tile + chunk_off<G>(n, hh * (G::CPR / 2) + kk));
+      acc[hb] = Mma::mma(qf[hb][kk], bf[kk], kk == 0 ? f32x16_t{} : acc[hb]);
+    if (next) bf[kk] = read_frag<Mma, G>(tile, n, hh, kk);
     if (prev) {
 #pragma unroll
       for (int sl = kk * EPI_SLICES / NKK; sl < (kk + 1) * EPI_SLICES / NKK; ++sl) epi_slice<HB>(pacc, wv, sl, p);

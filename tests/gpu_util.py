@@ -10,9 +10,12 @@ import workloads as W
 
 
 def dev(prob: W.Problem, device="cuda"):
-    """Returns dict(q, k, w, q_pos, k_len, k_scale) of device tensors holding the same bytes."""
+    """Returns dict(q, k, w, q_pos, k_len, k_scale, q_scale) of device tensors holding the same
+    bytes."""
     if prob.q_dtype == W.BF16:
         q = torch.from_numpy(prob.q.view(np.int16)).view(torch.bfloat16)
+    elif prob.q_dtype == W.FP8_E4M3:
+        q = torch.from_numpy(prob.q).view(torch.float8_e4m3fn)
     else:
         q = torch.from_numpy(prob.q)
     if prob.k_dtype == W.BF16:
@@ -26,6 +29,9 @@ def dev(prob: W.Problem, device="cuda"):
                k_len=torch.from_numpy(prob.k_len).to(device), k_scale=None)
     if prob.k_scale is not None:
         out["k_scale"] = torch.from_numpy(prob.k_scale).to(device)
+    out["q_scale"] = None
+    if getattr(prob, "q_scale", None) is not None:
+        out["q_scale"] = torch.from_numpy(prob.q_scale).to(device)
     return out
 
 

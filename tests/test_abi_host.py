@@ -49,7 +49,8 @@ def test_strerror(L):
 
 def _problem(**kw):
     base = dict(B=1, T=64, H=64, D=128, N=64, q_dtype=idx.BF16, k_dtype=idx.BF16,
-                q=0x10000, k=0x20000, k_scale=None, w=0x30000, q_pos=0x40000, k_len=None)
+                q=0x10000, k=0x20000, k_scale=None, w=0x30000, q_pos=0x40000, k_len=None,
+                q_scale=None)
     base.update(kw)
     return idx.Problem(**base)
 
@@ -84,7 +85,17 @@ def test_invalid_arguments(L):
 def test_unsupported_shapes(L):
     assert _call(L, _problem(D=48)) == -2
     assert _call(L, _problem(H=129)) == -2
-    assert _call(L, _problem(q_dtype=idx.FP8_E4M3)) == -2
+    # FP8 queries: need q_scale, FP8 keys and D >= 64, and only the dense entry points take them
+    assert _call(L, _problem(q_dtype=idx.FP8_E4M3)) == -1
+    assert _call(L, _problem(q_dtype=idx.FP8_E4M3, q_scale=0x70000)) == -2
+    assert _call(L, _problem(q_dtype=idx.FP8_E4M3, q_scale=0x70000, k_dtype=idx.FP8_E4M3,
+                             k_scale=0x78000, D=32)) == -2
+    assert _call(L, _problem(q_dtype=idx.FP8_E4M3, q_scale=0x70002, k_dtype=idx.FP8_E4M3,
+                             k_scale=0x78000)) == -3
+    p8 = _problem(q_dtype=idx.FP8_E4M3, q_scale=0x70000, k_dtype=idx.FP8_E4M3, k_scale=0x78000)
+    assert L.idx_group_proxy_refine(ctypes.byref(p8), 8, 4, 16, 0x50000, None, None, 0x60000,
+                                    1 << 40, None) == -2
+    assert L.idx_group_proxy_reuse(ctypes.byref(p8), 8, 4, 0x50000, None, 0x60000, 1 << 40, None) == -2
     assert _call(L, _problem(k_dtype=7)) == -2
 
 
