@@ -310,14 +310,16 @@ def pool_keys(prob, b: int, block_size: int) -> np.ndarray:
     """Pooled block keys ([HISA] scores pooled representations of key blocks; it does not say
     which pooling). Reading: the mean of the keys of each block of `block_size` consecutive tokens, over the tokens that
     exist in the cache (the last block may be partial). Like the proxy query it is an indexer
-    input stored in the key format: fp32 sum in ascending token order from +0, one fp32
-    division by the token count, nearest-even to bf16 for bf16 keys (fp32 keys stay fp32).
+    input stored in a key format: fp32 sum in ascending token order from +0, one fp32
+    division by the token count, nearest-even to bf16 for bf16 and FP8 keys (fp32 keys stay
+    fp32). An FP8 key enters the sum as its fp32 value decode(byte) * scale (one fp32 multiply).
     Returns the pooled keys in storage form [NB,D]."""
-    if prob.k_dtype == FP8_E4M3:
-        raise ValueError("block pooling is defined for bf16 and fp32 key caches")
     L = int(prob.k_len[b])
     if prob.k_dtype == BF16:
         kf = (np.asarray(prob.k[b, :L], np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    elif prob.k_dtype == FP8_E4M3:
+        kf = (e4m3fn_bits_to_f64(prob.k[b, :L]).astype(np.float32) *
+              np.asarray(prob.k_scale[b, :L], np.float32)[:, None]).astype(np.float32)
     else:
         kf = np.asarray(prob.k[b, :L], np.float32)
     NB = (L + block_size - 1) // block_size
@@ -333,7 +335,7 @@ def pool_keys(prob, b: int, block_size: int) -> np.ndarray:
         for s in range(nfull * block_size, L):
             acc1 = (acc1 + kf[s]).astype(np.float32)
         out[nfull] = (acc1 / np.float32(L - nfull * block_size)).astype(np.float32)
-    return f32_to_bf16_bits_rne(out) if prob.k_dtype == BF16 else out
+    return out if prob.k_dtype == F32 else f32_to_bf16_bits_rne(out)
 
 
 def block_row(inp: Inputs, b: int, t: int, k: int, block_size: int, n_keep: int,

@@ -228,3 +228,50 @@ def test_group_block_candidates_are_kept_blocks(hier):
         for t in oracle.group_members(hier.T, G, g):
             sel = g_idx[b, t][g_idx[b, t] >= 0]
             assert set(sel.tolist()) <= set(gs["tokens"].tolist())
+
+
+# ---------------------------------------------------------------- FP8 key caches in the block paths
+
+def test_pool_fp8_unit_scales_equal_bf16_pool():
+    # every E4M3 value is a bf16 value: with unit scales the FP8 cache pools to exactly what the
+    # bf16 cache of the same values pools to
+    rng = np.random.default_rng(31)
+    p8 = W.make_decode(1, 300, T=2, seed=32)
+    b8 = rng.integers(0, 256, size=p8.k.shape).astype(np.uint8)
+    p8.k = np.where((b8 & 0x7F) == 0x7F, 0x38, b8).astype(np.uint8)
+    p8.k_scale = np.ones_like(p8.k_scale)
+    vals = oracle.e4m3fn_bits_to_f64(p8.k).astype(np.float32)
+    pb = W.Problem(p8.q, p8.q_dtype, oracle.f32_to_bf16_bits_rne(vals).reshape(p8.k.shape), W.BF16, None,
+                   p8.w, p8.q_pos, p8.k_len)
+    for Bs in (1, 7, 128):
+        assert np.array_equal(oracle.pool_keys(p8, 0, Bs), oracle.pool_keys(pb, 0, Bs))
+
+
+def test_pool_fp8_hand_block():
+    # tokens (1, 2) * 0.5 and (-1, 2) * 3 -> fp32 values (0.5, 1) and (-3, 6): mean (-1.25, 3.5)
+    p = W.make_decode(1, 2, T=1, H=1, D=2, seed=33)
+    p.k = np.array([[[0x38, 0x40], [0xb8, 0x40]]], np.uint8)
+    p.k_scale = np.array([[0.5, 3.0]], np.float32)
+    got = oracle.bf16_bits_to_f64(oracle.pool_keys(p, 0, 2))
+    assert got.tolist() == [[-1.25, 3.5]]
+
+
+def test_fp8_block_keep_all_is_dense():
+    p = W.make_decode(2, 700, T=2, seed=34, k_len=[700, 333])
+    k = 100
+    inp = oracle.Inputs(p)
+    for b in range(2):
+        pooled = oracle.pool_keys(p, b, 16)
+        for t in range(2):
+            r = oracle.block_row(inp, b, t, k, 16, 10 ** 4, pooled)
+            d = oracle.dense_row(inp, b, t, k)
+            assert np.array_equal(np.sort(r["ids"]), np.sort(d["ids"]))
+
+
+def test_fp8_group_block_keep_all_is_dense():
+    p = W.make_decode(1, 900, T=2, seed=35)
+    k = 64
+    out, _, _ = oracle.group_block(p, k, 2, 32, 10 ** 4)
+    ref, _ = oracle.dense(p, k)
+    for t in range(2):
+        assert set(out[0, t].tolist()) == set(ref[0, t].tolist())
