@@ -151,23 +151,57 @@ def gblock_refine_pairs(prob, G, Bs, keep):
     group's proxy) blocks of Bs tokens per member, cut to the member's prefix (the partial last
     block counted whole, as for the block path)."""
     import numpy as np
-    pos = prob.q_pos[0].astype(np.int64)
-    L = int(prob.k_len[0])
-    NB = -(-L // Bs)
     n = 0
-    for g in range((prob.T + G - 1) // G):
-        mem = pos[g * G:min(prob.T, g * G + G)]
-        nk = min(keep, min(int(mem.max()) // Bs + 1, NB))
-        n += int(np.minimum(nk * Bs, np.minimum(mem + 1, L)).sum())
+    for b in range(prob.B):
+        pos = prob.q_pos[b].astype(np.int64)
+        L = int(prob.k_len[b])
+        NB = -(-L // Bs)
+        for g in range((prob.T + G - 1) // G):
+            mem = pos[g * G:min(prob.T, g * G + G)]
+            if mem.max() < 0:
+                continue
+            nk = min(keep, min(int(mem.max()) // Bs + 1, NB))
+            n += int(np.clip(np.minimum(nk * Bs, np.minimum(mem + 1, L)), 0, None).sum())
     return n
 
 
 def block_pairs(prob, Bs, keep):
+    """(coarse pairs: queries x eligible pooled blocks, refine pairs: queries x kept tokens)."""
     import numpy as np
-    pos = prob.q_pos[0].astype(np.int64)
-    NB = -(-int(prob.k_len[0]) // Bs)
-    coarse = int(np.minimum(pos // Bs + 1, NB).sum())
-    refine = int(np.minimum(np.minimum(pos // Bs + 1, NB), keep).sum() * Bs)
+    coarse = refine = 0
+    for b in range(prob.B):
+        pos = prob.q_pos[b].astype(np.int64)
+        NB = -(-int(prob.k_len[b]) // Bs)
+        elig = np.where(pos < 0, 0, np.minimum(pos // Bs + 1, NB))
+        coarse += int(elig.sum())
+        refine += int(np.minimum(elig, keep).sum() * Bs)
+    return coarse, refine
+
+
+def filtered_decode_bytes(prob, spec):
+    """Algorithmic HBM bytes of one block-filtered decode step: (coarse: each sequence's pooled
+    block keys read once, bf16 or fp32 for fp32 caches; refine: each token list's keys, + its
+    fp32 scale for FP8 caches, read once: a list per query for the block path, per group for the
+    group path, of min(keep, eligible blocks) blocks cut to the cache)."""
+    import numpy as np
+    import workloads as W
+    Bs, keep = spec["block_size"], spec["n_blocks_keep"]
+    G = spec.get("group_size", 1) if spec["op"] == "gblock" else 1
+    kb = {W.F32: 4, W.BF16: 2, W.FP8_E4M3: 1}[prob.k_dtype]
+    tok = prob.D * kb + (4 if prob.k_dtype == W.FP8_E4M3 else 0)
+    pooled_b = prob.D * (4 if prob.k_dtype == W.F32 else 2)
+    coarse = refine = 0
+    for b in range(prob.B):
+        pos = prob.q_pos[b].astype(np.int64)
+        L = int(prob.k_len[b])
+        NB = -(-L // Bs)
+        if pos.max() >= 0:
+            coarse += min(NB, int(pos.max()) // Bs + 1) * pooled_b
+        for g in range((prob.T + G - 1) // G):
+            top = int(pos[g * G:min(prob.T, g * G + G)].max())
+            if top >= 0:
+                nk = min(keep, min(top // Bs + 1, NB))
+                refine += min(nk * Bs, L) * tok
     return coarse, refine
 
 
@@ -231,18 +265,21 @@ def cpu_oracle_baseline(name, spec, prob, budget_s=12.0):
     elif op == "gblock":
         G, Bs, keep = spec["group_size"], spec["block_size"], spec["n_blocks_keep"]
         NG = (T + G - 1) // G
-        pooled = oracle.pool_keys(prob, 0, Bs)
+        pooled = {}
         stride = max(1, NG // 64)
-        for g in [g for off in range(stride) for g in range(NG - 1 - off, -1, -stride)]:
-            gs = oracle.group_block_scan(inp, 0, g, G, Bs, keep, pooled)
+        for b, g in [(b, g) for off in range(stride) for g in range(NG - 1 - off, -1, -stride)
+                     for b in range(B)]:
+            if b not in pooled:
+                pooled[b] = oracle.pool_keys(prob, b, Bs)
+            gs = oracle.group_block_scan(inp, b, g, G, Bs, keep, pooled[b])
             for t in oracle.group_members(T, G, g):
-                oracle.refine_row(inp, 0, t, spec["k"], gs["tokens"])
-                done_pairs += inp.P(0, t)
+                oracle.refine_row(inp, b, t, spec["k"], gs["tokens"])
+                done_pairs += inp.P(b, t)
                 rows += 1
             if time.perf_counter() - t0 > budget_s:
                 break
-        sample = (f"{rows} query rows of {T} in whole groups, interleaved with stride {stride} "
-                  "(pooling once, proxy block scan + refine)")
+        sample = (f"{rows} query rows of {B * T} in whole groups, interleaved with stride {stride} "
+                  f"(pooling each of {len(pooled)} sequences once, proxy block scan + refine)")
     elif op == "given":
         G = spec["group_size"]
         banks = W.make_banks(prob, G, spec["n_cand"], 0)
@@ -257,15 +294,19 @@ def cpu_oracle_baseline(name, spec, prob, budget_s=12.0):
         sample = f"{rows} query rows of {T} (interleaved with stride {stride}), refine over the given bank"
     else:
         Bs, keep = spec["block_size"], spec["n_blocks_keep"]
-        pooled = oracle.pool_keys(prob, 0, Bs)
+        pooled = {}
         stride = max(1, T // 128)
-        for t in [t for off in range(stride) for t in range(T - 1 - off, -1, -stride)]:
-            oracle.block_row(inp, 0, t, spec["k"], Bs, keep, pooled)
-            done_pairs += inp.P(0, t)
+        for b, t in [(b, t) for off in range(stride) for t in range(T - 1 - off, -1, -stride)
+                     for b in range(B)]:
+            if b not in pooled:
+                pooled[b] = oracle.pool_keys(prob, b, Bs)
+            oracle.block_row(inp, b, t, spec["k"], Bs, keep, pooled[b])
+            done_pairs += inp.P(b, t)
             rows += 1
             if time.perf_counter() - t0 > budget_s:
                 break
-        sample = f"{rows} query rows of {T} (interleaved with stride {stride}), pooling + coarse + refine"
+        sample = (f"{rows} query rows of {B * T} (interleaved with stride {stride}), pooling each of "
+                  f"{len(pooled)} sequences once + coarse + refine")
     dt = time.perf_counter() - t0
     return {"value": done_pairs / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
             "sample": sample + f"; {dt:.1f} s; dense-equivalent pairs", **host_info(threads)}
@@ -333,6 +374,12 @@ class Run:
         else:
             need = idx.workspace_bytes(idx.OP_BLOCK, p, k, spec["block_size"], spec["n_blocks_keep"])
         self.ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+        # pooled block keys kept beside the cache (a decoding server pools a block once, when it
+        # is complete): pooled here once, before timing; the pooling of the whole cache is timed
+        # on its own
+        self.pooled = None
+        if spec.get("pooled"):
+            self.pooled = idx.block_pool(t["k"], spec["block_size"], k_len=t["k_len"], k_scale=t["k_scale"])
 
     def step(self):
         import sparse_attention_indexer_02_amd as idx
@@ -348,7 +395,8 @@ class Run:
         elif op == "gblock":
             idx.group_block_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
                                    group_size=spec["group_size"], block_size=spec["block_size"],
-                                   n_blocks_keep=spec["n_blocks_keep"], **kw)
+                                   n_blocks_keep=spec["n_blocks_keep"], k_scale=t["k_scale"],
+                                   pooled=self.pooled, **kw)
         elif op == "reuse":
             idx.group_proxy_reuse(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
                                   group_size=spec["group_size"], k_scale=t["k_scale"], **kw)
@@ -358,7 +406,8 @@ class Run:
         else:
             idx.block_coarse_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
                                     block_size=spec["block_size"],
-                                    n_blocks_keep=spec["n_blocks_keep"], **kw)
+                                    n_blocks_keep=spec["n_blocks_keep"], k_scale=t["k_scale"],
+                                    pooled=self.pooled, **kw)
 
     def time(self, steps, warmup):
         """Mean step time (HIP events around exactly `steps` steps after `warmup` untimed ones)
@@ -390,6 +439,17 @@ class Run:
         log(f"[bench] {self.name}: {self.ms_step:.4f} ms/step; per-kernel ms/step: " + ", ".join(
             f"{n} {ms / steps:.3f} ({c // max(1, steps)} launches)"
             for n, (ms, c) in self.kernels.items() if c))
+        self.pool_ms = None
+        if self.pooled is not None:
+            t, spec = self.t, self.spec
+            e0.record()
+            for _ in range(steps):
+                idx.block_pool(t["k"], spec["block_size"], k_len=t["k_len"], k_scale=t["k_scale"],
+                               out=self.pooled)
+            e1.record()
+            torch.cuda.synchronize()
+            self.pool_ms = e0.elapsed_time(e1) / steps
+            log(f"[bench] {self.name}: pooling the whole cache (outside the step) {self.pool_ms:.4f} ms")
 
     def _mfma(self, kernel, flops, **extra):
         import workloads as W
@@ -428,6 +488,33 @@ class Run:
             roof = self._mfma("score_kernel", 2.0 * prob.H * prob.D * (pp + rp))
             cfg.update(group_size=spec["group_size"], n_cand=spec["n_cand"],
                        algorithmic_pairs_per_step=pp + rp)
+        elif spec.get("pooled"):
+            # block filter at decode: the decode scan streams the kept tokens once per list, bound
+            # by their read; the coarse scan of the pooled keys is reported beside it
+            cb, rb = filtered_decode_bytes(prob, spec)
+            ms, n = self.kernels["decode_scan"]
+            if n:
+                kern, per_launch = "decode_scan_kernel", rb / (n / self.steps)
+                achieved = per_launch / (ms / n * 1e-3) / 1e9
+                extra = {"per_launch": f"{per_launch:.4g} B (kept tokens' keys and scales)"}
+            else:
+                ms, n = self.kernels["score"]
+                kern = "score_kernel"
+                achieved = (cb + rb) / (ms / self.steps * 1e-3) / 1e9
+                extra = {"per_step": f"{cb + rb:.4g} B over {n // self.steps} launches (pooled keys and "
+                                     "kept tokens)"}
+            cms, cn = self.kernels["score"]
+            roof = {"bound": "hbm", "kernel": kern, "achieved": achieved,
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                    "traffic": measured_traffic(self.name, kern), "mean_launch_ms": ms / n, **extra,
+                    "coarse_scan": {"bytes_per_step": cb, "ms_per_step": cms / self.steps,
+                                    "launches_per_step": cn // self.steps}}
+            G = spec.get("group_size", 1) if op == "gblock" else 1
+            cfg.update(block_size=spec["block_size"], n_blocks_keep=spec["n_blocks_keep"],
+                       pooled_keys="kept beside the cache, not pooled in the step",
+                       pool_whole_cache_ms=self.pool_ms)
+            if op == "gblock":
+                cfg.update(group_size=G)
         elif op == "gblock":
             G, Bs, keep = spec["group_size"], spec["block_size"], spec["n_blocks_keep"]
             rp = gblock_refine_pairs(prob, G, Bs, keep)
@@ -494,7 +581,7 @@ class Run:
 
     def free(self):
         import torch
-        for a in ("t", "out_idx", "out_sc", "ws", "banks"):
+        for a in ("t", "out_idx", "out_sc", "ws", "banks", "pooled"):
             if hasattr(self, a):
                 delattr(self, a)
         torch.cuda.empty_cache()

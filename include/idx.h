@@ -145,12 +145,32 @@ int idx_group_proxy_refine(const idx_problem* p, int32_t k, int32_t group_size, 
  *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
  *   out_blocks [B, T, n_blocks_keep] int32 (optional): kept block ids in ascending order, -1
  *              padded.
- * Keys must be IDX_BF16 or IDX_F32 (IDX_ERR_UNSUPPORTED for fp8). Requires
- * ceil(N / block_size) <= 65536 and n_blocks_keep <= 32767. With n_blocks_keep >= the number of
- * eligible blocks the result equals idx_score_topk's. */
+ * Keys may be IDX_BF16, IDX_F32 or IDX_FP8_E4M3: an FP8 key enters its block's mean as its fp32
+ * value decode(byte) * k_scale (one fp32 multiply), and the pooled keys are bf16 (fp32 for fp32
+ * keys); the token refine scores the FP8 keys themselves. Requires ceil(N / block_size) <= 65536
+ * and n_blocks_keep <= 32767. With n_blocks_keep >= the number of eligible blocks the result
+ * equals idx_score_topk's. */
 int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
                             int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
                             int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream);
+
+/* The pooled block keys of idx_block_coarse_refine for the whole cache, written to `pooled`
+ * [B, ceil(N / block_size), D]: bf16 for IDX_BF16 and IDX_FP8_E4M3 keys, fp32 for IDX_F32 keys (a
+ * block past k_len[b] is written as zeros and never scored). Only the key fields of *p (B, N, D,
+ * k_dtype, k, k_scale, k_len) are read. A caller that keeps the pooled keys beside its key cache
+ * (a decoding server pools a block once it is complete) passes them to the *_pooled entry points
+ * below instead of pooling the whole cache on every call ("HISA ...", abstract: block-level
+ * pooled representations of the cache). Errors: IDX_ERR_INVALID_ARG (null k, pooled or
+ * required k_scale, block_size < 1), IDX_ERR_UNSUPPORTED (D not 32, 64 or 128),
+ * IDX_ERR_ALIGN (k or pooled not 16-byte aligned). */
+int idx_block_pool(const idx_problem* p, int32_t block_size, void* pooled, void* stream);
+
+/* idx_block_coarse_refine with the caller's pooled keys (as idx_block_pool writes them) in place
+ * of pooling inside the call; `pooled` is required and 16-byte aligned. Same results. */
+int idx_block_coarse_refine_pooled(const idx_problem* p, int32_t k, int32_t block_size,
+                                   int32_t n_blocks_keep, const void* pooled, int32_t* out_idx,
+                                   float* out_score, int32_t* out_blocks, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* Group-shared scan without refine ("PIVOT ...", abstract; PIVOT-Reuse: the proxy's top-k is
  * shared across the group). Groups and proxies are those of idx_group_proxy_refine. The proxy
@@ -172,15 +192,24 @@ int idx_group_proxy_reuse(const idx_problem* p, int32_t k, int32_t group_size, i
  *   out_idx [B, T, k] int32 (required), out_score [B, T, k] fp32 (optional),
  *   out_blocks [B, ceil(T/group_size), n_blocks_keep] int32 (optional): each group's kept blocks
  *              in ascending order, -1 padded.
- * Keys must be IDX_BF16 or IDX_F32. Requires ceil(N / block_size) <= 65536 and
- * n_blocks_keep <= 32767. group_size = 1 gives idx_block_coarse_refine's result; keeping every
- * block gives idx_score_topk's. Its workspace size is idx_group_block_workspace_bytes(...). */
+ * Keys may be IDX_BF16, IDX_F32 or IDX_FP8_E4M3 (pooled as in idx_block_coarse_refine). Requires
+ * ceil(N / block_size) <= 65536 and n_blocks_keep <= 32767. group_size = 1 gives
+ * idx_block_coarse_refine's result; keeping every block gives idx_score_topk's. In decode,
+ * group_size = T filters the cache once for the queries of one multi-token-prediction step. Its
+ * workspace size is idx_group_block_workspace_bytes(...). */
 int idx_group_block_refine(const idx_problem* p, int32_t k, int32_t group_size, int32_t block_size,
                            int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
                            int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes of idx_group_block_refine for the same arguments (only the shape fields of *p
- * are read); 0 for invalid arguments. */
+/* idx_group_block_refine with the caller's pooled keys (as idx_block_pool writes them) in place
+ * of pooling inside the call; `pooled` is required and 16-byte aligned. Same results. */
+int idx_group_block_refine_pooled(const idx_problem* p, int32_t k, int32_t group_size,
+                                  int32_t block_size, int32_t n_blocks_keep, const void* pooled,
+                                  int32_t* out_idx, float* out_score, int32_t* out_blocks, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* Workspace bytes of idx_group_block_refine (and of its _pooled form) for the same arguments
+ * (only the shape fields of *p are read); 0 for invalid arguments. */
 size_t idx_group_block_workspace_bytes(const idx_problem* p, int32_t k, int32_t group_size,
                                        int32_t block_size, int32_t n_blocks_keep);
 
@@ -207,7 +236,8 @@ int idx_refine_given(const idx_problem* p, int32_t k, int32_t group_size, const 
                      void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by one call. op = IDX_OP_*; p1, p2 = (group_size, n_cand) for
- * IDX_OP_GROUP and IDX_OP_REFINE, (block_size, n_blocks_keep) for IDX_OP_BLOCK, (group_size,
+ * IDX_OP_GROUP and IDX_OP_REFINE, (block_size, n_blocks_keep) for IDX_OP_BLOCK (also enough for
+ * idx_block_coarse_refine_pooled), (group_size,
  * ignored) for IDX_OP_REUSE, ignored for IDX_OP_SCORE_TOPK.
  * Only the shape fields of *p are read (pointers may be NULL). Returns 0 for invalid arguments. */
 size_t idx_workspace_bytes(int op, const idx_problem* p, int32_t k, int32_t p1, int32_t p2);

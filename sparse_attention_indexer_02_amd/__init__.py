@@ -29,14 +29,16 @@ import torch
 
 __all__ = ["F32", "BF16", "FP8_E4M3", "IdxError", "lib", "score_topk", "score_topk_noalloc",
            "group_proxy_refine",
-           "block_coarse_refine", "refine_given", "group_proxy_reuse", "group_block_refine", "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
+           "block_coarse_refine", "refine_given", "group_proxy_reuse", "group_block_refine", "block_pool",
+           "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OP_SCORE_TOPK, OP_GROUP, OP_BLOCK, OP_REFINE, OP_REUSE = 0, 1, 2, 3, 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidx.so")
 EXPORTS = ["idx_score_topk", "idx_score_topk_noalloc", "idx_group_proxy_refine", "idx_block_coarse_refine",
            "idx_refine_given", "idx_group_proxy_reuse", "idx_group_block_refine",
-           "idx_group_block_workspace_bytes", "idx_workspace_bytes", "idx_strerror", "idx_timer_enable", "idx_timer_read"]
+           "idx_group_block_workspace_bytes", "idx_workspace_bytes", "idx_strerror", "idx_timer_enable",
+           "idx_timer_read", "idx_block_pool", "idx_block_coarse_refine_pooled", "idx_group_block_refine_pooled"]
 
 
 class IdxError(RuntimeError):
@@ -71,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.idx_refine_given.argtypes = [P, i32, i32, vp, vp, i32, vp, vp, vp, sz, vp]
         L.idx_group_proxy_reuse.argtypes = [P, i32, i32, vp, vp, vp, sz, vp]
         L.idx_group_block_refine.argtypes = [P, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.idx_block_pool.argtypes = [P, i32, vp, vp]
+        L.idx_block_coarse_refine_pooled.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.idx_group_block_refine_pooled.argtypes = [P, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.idx_group_block_workspace_bytes.argtypes = [P, i32, i32, i32, i32]
         L.idx_group_block_workspace_bytes.restype = sz
         L.idx_workspace_bytes.argtypes = [ctypes.c_int, P, i32, i32, i32]
@@ -82,7 +87,8 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_int32)]
         for f in ("idx_score_topk", "idx_score_topk_noalloc", "idx_group_proxy_refine", "idx_block_coarse_refine",
                   "idx_refine_given", "idx_group_proxy_reuse", "idx_group_block_refine",
-                  "idx_timer_enable", "idx_timer_read"):
+                  "idx_timer_enable", "idx_timer_read", "idx_block_pool",
+                  "idx_block_coarse_refine_pooled", "idx_group_block_refine_pooled"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -237,11 +243,34 @@ def group_proxy_reuse(q, k, w, q_pos, topk: int = 2048, group_size: int = 16, k_
     return out_idx, out_score
 
 
+def pooled_shape(k, block_size):
+    """Shape and dtype of the pooled block keys of a key cache k [B,N,D]."""
+    B, N, D = k.shape
+    return (B, (N + block_size - 1) // block_size, D), (torch.float32 if k.dtype == torch.float32 else torch.bfloat16)
+
+
+def block_pool(k, block_size: int = 128, k_len=None, k_scale=None, out=None, stream=None):
+    """Pooled block keys of the whole cache (idx_block_pool): bf16 [B, ceil(N/Bs), D] for bf16 and
+    FP8 keys, fp32 for fp32 keys."""
+    B, N, D = k.shape
+    kc = _kcode(k)
+    if kc == FP8_E4M3 and (k_scale is None or k_scale.dtype != torch.float32):
+        raise IdxError("fp8 keys need k_scale float32 [B,N]")
+    shape, dt = pooled_shape(k, block_size)
+    if out is None:
+        out = torch.empty(shape, dtype=dt, device=k.device)
+    p = Problem(B, 1, 1, D, N, BF16, kc, None, _ptr(k), _ptr(k_scale) if kc == FP8_E4M3 else None, None,
+                None, _ptr(k_len), None)
+    _check(lib().idx_block_pool(ctypes.byref(p), block_size, _ptr(out), _stream(k, stream)), "idx_block_pool")
+    return out
+
+
 def group_block_refine(q, k, w, q_pos, topk: int = 2048, group_size: int = 16,
                        block_size: int = 128, n_blocks_keep: int = 128, k_len=None, k_scale=None,
                        out_idx=None, out_score=None, want_score: bool = True,
-                       return_blocks: bool = False, workspace=None, stream=None):
-    """Block-filtered group proxy with per-query refine (idx_group_block_refine)."""
+                       return_blocks: bool = False, workspace=None, stream=None, pooled=None):
+    """Block-filtered group proxy with per-query refine (idx_group_block_refine, or
+    idx_group_block_refine_pooled when the pooled keys are given)."""
     p = make_problem(q, k, w, q_pos, k_len, k_scale)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     blocks = None
@@ -251,10 +280,17 @@ def group_block_refine(q, k, w, q_pos, topk: int = 2048, group_size: int = 16,
     need = int(lib().idx_group_block_workspace_bytes(ctypes.byref(p), topk, group_size, block_size,
                                                      n_blocks_keep))
     ws = _workspace(q, need, workspace)
-    _check(lib().idx_group_block_refine(ctypes.byref(p), topk, group_size, block_size, n_blocks_keep,
-                                        _ptr(out_idx), _ptr(out_score), _ptr(blocks), _ptr(ws),
-                                        ws.numel() * ws.element_size(), _stream(q, stream)),
-           "idx_group_block_refine")
+    if pooled is None:
+        _check(lib().idx_group_block_refine(ctypes.byref(p), topk, group_size, block_size, n_blocks_keep,
+                                            _ptr(out_idx), _ptr(out_score), _ptr(blocks), _ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(q, stream)),
+               "idx_group_block_refine")
+    else:
+        _check(lib().idx_group_block_refine_pooled(ctypes.byref(p), topk, group_size, block_size,
+                                                   n_blocks_keep, _ptr(pooled), _ptr(out_idx),
+                                                   _ptr(out_score), _ptr(blocks), _ptr(ws),
+                                                   ws.numel() * ws.element_size(), _stream(q, stream)),
+               "idx_group_block_refine_pooled")
     return out_idx, out_score, blocks
 
 
@@ -287,9 +323,10 @@ def refine_given(q, k, w, q_pos, cand, cand_cnt=None, topk: int = 2048, group_si
 def block_coarse_refine(q, k, w, q_pos, topk: int = 2048, block_size: int = 128,
                         n_blocks_keep: int = 128, k_len=None, out_idx=None, out_score=None,
                         want_score: bool = True, return_blocks: bool = False, workspace=None,
-                        stream=None):
-    """Block-pooled coarse filter + token refine (idx_block_coarse_refine)."""
-    p = make_problem(q, k, w, q_pos, k_len, None)
+                        stream=None, k_scale=None, pooled=None):
+    """Block-pooled coarse filter + token refine (idx_block_coarse_refine, or
+    idx_block_coarse_refine_pooled when the pooled keys are given)."""
+    p = make_problem(q, k, w, q_pos, k_len, k_scale)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     blocks = None
     if return_blocks:
@@ -297,10 +334,17 @@ def block_coarse_refine(q, k, w, q_pos, topk: int = 2048, block_size: int = 128,
                              device=q.device)
     need = workspace_bytes(OP_BLOCK, p, topk, block_size, n_blocks_keep)
     ws = _workspace(q, need, workspace)
-    _check(lib().idx_block_coarse_refine(ctypes.byref(p), topk, block_size, n_blocks_keep,
-                                         _ptr(out_idx), _ptr(out_score), _ptr(blocks), _ptr(ws),
-                                         ws.numel() * ws.element_size(), _stream(q, stream)),
-           "idx_block_coarse_refine")
+    if pooled is None:
+        _check(lib().idx_block_coarse_refine(ctypes.byref(p), topk, block_size, n_blocks_keep,
+                                             _ptr(out_idx), _ptr(out_score), _ptr(blocks), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(q, stream)),
+               "idx_block_coarse_refine")
+    else:
+        _check(lib().idx_block_coarse_refine_pooled(ctypes.byref(p), topk, block_size, n_blocks_keep,
+                                                    _ptr(pooled), _ptr(out_idx), _ptr(out_score),
+                                                    _ptr(blocks), _ptr(ws), ws.numel() * ws.element_size(),
+                                                    _stream(q, stream)),
+               "idx_block_coarse_refine_pooled")
     return out_idx, out_score, blocks
 
 

@@ -157,8 +157,69 @@ struct ReusePlan {
   size_t bytes;
 };
 
+int cu_count();
+
+struct DecodePlan {
+  int nchunk, chunk, sub, nsegs, cand_cap, pair, vn;
+  uint32_t* ccount;
+  uint32_t* shist;
+  uint32_t* cand_key;
+  uint32_t* cand_idx;
+  uint32_t* cand2_key;
+  uint32_t* cand2_idx;
+  size_t bytes;
+};
+
+// The decode scan's split and buffers for rows of vn slots (N, or the kept tokens of a block
+// list), `pair` queries per work-group.
+void carve_decode(DecodePlan& d, Carver& c, const idx_problem* p, int64_t vn, int pair) {
+  const int64_t rows = (int64_t)p->B * p->T;
+  const int pairs = (p->T + pair - 1) / pair;
+  // about one scan work-group per compute unit (each holds a whole unit's LDS), chunks of at
+  // least 1024 keys
+  int nchunk = std::max(1, (cu_count() + p->B * pairs - 1) / (p->B * pairs));
+  int chunk = (int)std::max<int64_t>(1024, (vn + nchunk - 1) / nchunk);
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk > DECODE_SUB) chunk = (chunk + DECODE_SUB - 1) / DECODE_SUB * DECODE_SUB;
+  d.pair = pair;
+  d.vn = (int)vn;
+  d.chunk = chunk;
+  d.nchunk = (int)((vn + chunk - 1) / chunk);
+  d.sub = std::min(chunk, DECODE_SUB);
+  d.nsegs = (int)((vn + d.sub - 1) / d.sub);
+  d.cand_cap = (int)rstride(vn);
+  d.ccount = c.take<uint32_t>((size_t)rows * d.nsegs);
+  d.shist = c.take<uint32_t>((size_t)rows * d.nsegs * (DECODE_BINS / 2));
+  d.cand_key = c.take<uint32_t>((size_t)rows * d.cand_cap);
+  d.cand_idx = c.take<uint32_t>((size_t)rows * d.cand_cap);
+  d.cand2_key = c.take<uint32_t>((size_t)rows * d.cand_cap);
+  d.cand2_idx = c.take<uint32_t>((size_t)rows * d.cand_cap);
+}
+
+DecodePlan plan_decode(const idx_problem* p, void* ws) {
+  DecodePlan d;
+  Carver c(ws);
+  carve_decode(d, c, p, p->N, 2);
+  d.bytes = c.off + kAlign;
+  return d;
+}
+
+// The decode scan over the kept blocks applies to decode shapes with blocks of 16 tokens or more
+// (a power of two).
+bool blocks_by_decode(const idx_problem* p, int Bs, int keep) {
+  return decode_blocks_supported(p->q_dtype, p->k_dtype, p->H, p->D, p->T, p->N, Bs, keep);
+}
+
+int log2i(int v) {
+  int r = 0;
+  while ((1 << (r + 1)) <= v) ++r;
+  return r;
+}
+
 struct GroupBlockPlan {
   int NG, NB, chunkP, chunkG;
+  bool dec;            // members refine by the decode scan over the group's kept blocks
+  DecodePlan dp;
   void* pq;
   float* pw;
   int32_t* ppos;
@@ -222,30 +283,57 @@ GroupPlan plan_group(const idx_problem* p, int G, int C, void* ws, int32_t* out_
   return g;
 }
 
+int cu_count();
+
+// Pooled block keys are fp32 for fp32 key caches and bf16 for bf16 and FP8 caches.
+int pooled_dtype(int k_dtype) { return k_dtype == IDX_F32 ? IDX_F32 : IDX_BF16; }
+
+// The block path refines each query's kept tokens either with the union kernel (a work-group per
+// tile of queries streams the union of their kept blocks) or, for FP8 key caches and for
+// problems with too few query tiles to cover the CUs (decode: a few queries per sequence), as
+// per-query token lists through the list-mode score kernel, whose key ranges split across
+// work-groups.
+bool block_by_lists(const idx_problem* p) {
+  const int qt = score_queries_per_tile(p->H);
+  return p->k_dtype == IDX_FP8_E4M3 || (int64_t)p->B * ((p->T + qt - 1) / qt) < cu_count();
+}
+
 struct BlockPlan {
   int NB, chunkT1, chunkT2;
+  bool lists, dec;     // refine as token lists / by the decode scan over the kept blocks
+  DecodePlan dp;
   void* pooled;
   float* cscores;
   int32_t* blocks;
   int32_t* n_kept;
   float* rscores;
+  int32_t* list;       // lists route: [B*T][keep*Bs] kept tokens, ascending, and their counts
+  int32_t* cnt;
   int32_t* row_len;
   int32_t* meta;
   size_t bytes;
 };
 
-BlockPlan plan_block(const idx_problem* p, int Bs, int keep, void* ws, int32_t* out_blocks) {
+// pooled_in: the caller's pooled cache (then no pooled area is carved)
+BlockPlan plan_block(const idx_problem* p, int Bs, int keep, void* ws, int32_t* out_blocks,
+                     const void* pooled_in = nullptr) {
   BlockPlan b;
   Carver c(ws);
   b.NB = (p->N + Bs - 1) / Bs;
-  const size_t keb = p->k_dtype == IDX_BF16 ? 2 : 4;
-  b.pooled = c.take<uint8_t>((size_t)p->B * b.NB * p->D * keb);
+  b.dec = blocks_by_decode(p, Bs, keep);
+  b.lists = !b.dec && block_by_lists(p);
+  const size_t keb = pooled_dtype(p->k_dtype) == IDX_F32 ? 4 : 2;
+  b.pooled = pooled_in ? const_cast<void*>(pooled_in) : c.take<uint8_t>((size_t)p->B * b.NB * p->D * keb);
   b.chunkT1 = chunk_rows(p->B, rstride(b.NB) * 4, p->T);
   b.cscores = c.take<float>((size_t)p->B * b.chunkT1 * rstride(b.NB));
   b.blocks = out_blocks ? out_blocks : c.take<int32_t>((size_t)p->B * p->T * keep);
   b.n_kept = c.take<int32_t>((size_t)p->B * p->T);
-  b.chunkT2 = chunk_rows(p->B, rstride((int64_t)keep * Bs) * 4, p->T);
-  b.rscores = c.take<float>((size_t)p->B * b.chunkT2 * rstride((int64_t)keep * Bs));
+  const int64_t C = (int64_t)keep * Bs;
+  b.list = b.lists ? c.take<int32_t>((size_t)p->B * p->T * C) : nullptr;
+  b.cnt = b.lists ? c.take<int32_t>((size_t)p->B * p->T) : nullptr;
+  b.chunkT2 = b.dec ? 1 : chunk_rows(p->B, rstride(C) * 4, p->T);
+  b.rscores = b.dec ? nullptr : c.take<float>((size_t)p->B * b.chunkT2 * rstride(C));
+  if (b.dec) carve_decode(b.dp, c, p, C, 1);
   b.row_len = c.take<int32_t>((size_t)p->B * std::max(b.chunkT1, b.chunkT2));
   b.meta = c.take<int32_t>((size_t)p->B * std::max(b.chunkT1, b.chunkT2) * 4);
   b.bytes = c.off + kAlign;
@@ -268,43 +356,6 @@ int cu_count() {
     cached[dev] = v;
   }
   return cached[dev];
-}
-
-struct DecodePlan {
-  int nchunk, chunk, sub, nsegs, cand_cap;
-  uint32_t* ccount;
-  uint32_t* shist;
-  uint32_t* cand_key;
-  uint32_t* cand_idx;
-  uint32_t* cand2_key;
-  uint32_t* cand2_idx;
-  size_t bytes;
-};
-
-DecodePlan plan_decode(const idx_problem* p, void* ws) {
-  DecodePlan d;
-  Carver c(ws);
-  const int64_t rows = (int64_t)p->B * p->T;
-  const int pairs = (p->T + 1) / 2;
-  // about one scan work-group per compute unit (each holds a whole unit's LDS), chunks of at
-  // least 1024 keys
-  int nchunk = std::max(1, (cu_count() + p->B * pairs - 1) / (p->B * pairs));
-  int chunk = (int)std::max<int64_t>(1024, ((int64_t)p->N + nchunk - 1) / nchunk);
-  chunk = (chunk + 63) / 64 * 64;
-  if (chunk > DECODE_SUB) chunk = (chunk + DECODE_SUB - 1) / DECODE_SUB * DECODE_SUB;
-  d.chunk = chunk;
-  d.nchunk = (p->N + chunk - 1) / chunk;
-  d.sub = std::min(chunk, DECODE_SUB);
-  d.nsegs = (p->N + d.sub - 1) / d.sub;
-  d.cand_cap = (int)rstride(p->N);
-  d.ccount = c.take<uint32_t>((size_t)rows * d.nsegs);
-  d.shist = c.take<uint32_t>((size_t)rows * d.nsegs * (DECODE_BINS / 2));
-  d.cand_key = c.take<uint32_t>((size_t)rows * d.cand_cap);
-  d.cand_idx = c.take<uint32_t>((size_t)rows * d.cand_cap);
-  d.cand2_key = c.take<uint32_t>((size_t)rows * d.cand_cap);
-  d.cand2_idx = c.take<uint32_t>((size_t)rows * d.cand_cap);
-  d.bytes = c.off + kAlign;
-  return d;
 }
 
 void* align_ws(void* ws) {
@@ -368,11 +419,8 @@ TopkArgs topk_args(const float* scores, int64_t stride, const int32_t* row_len, 
 // ---------------------------------------------------------------------------------------------
 // entry points
 
-int decode_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score, void* ws,
-                size_t ws_bytes, hipStream_t s) {
-  DecodePlan pl = plan_decode(p, nullptr);
-  if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
-  pl = plan_decode(p, align_ws(ws));
+DecodeArgs decode_args(const idx_problem* p, const DecodePlan& pl, int32_t k, int32_t* out_idx,
+                       float* out_score) {
   DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = p->q; a.w = p->w; a.q_pos = p->q_pos;
@@ -384,9 +432,33 @@ int decode_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_sc
   a.cand2_key = pl.cand2_key; a.cand2_idx = pl.cand2_idx; a.cand_cap = pl.cand_cap;
   a.k = k;
   a.out_idx = out_idx; a.out_score = out_score;
+  a.pair = pl.pair; a.vn = pl.vn;
+  return a;
+}
+
+int run_decode(const DecodeArgs& a, hipStream_t s) {
   int st;
   if ((st = from_hip(timed("decode_scan", s, [&] { return launch_decode_scan(a, s); })))) return st;
   return from_hip(timed("decode_select", s, [&] { return launch_decode_select(a, s); }));
+}
+
+// The decode scan over each list's kept blocks (ascending, n_kept of them per list row), list
+// row b * n_groups + t / G for query (b, t).
+int refine_blocks_decode(const idx_problem* p, int32_t k, const DecodePlan& pl, const int32_t* blocks,
+                         const int32_t* n_kept, int keep, int Bs, int G, int n_groups, int32_t* out_idx,
+                         float* out_score, hipStream_t s) {
+  DecodeArgs a = decode_args(p, pl, k, out_idx, out_score);
+  a.blocks = blocks; a.n_kept = n_kept; a.keep_stride = keep; a.blk_shift = log2i(Bs);
+  a.group_size = G; a.n_groups = n_groups;
+  return run_decode(a, s);
+}
+
+int decode_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score, void* ws,
+                size_t ws_bytes, hipStream_t s) {
+  DecodePlan pl = plan_decode(p, nullptr);
+  if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
+  pl = plan_decode(p, align_ws(ws));
+  return run_decode(decode_args(p, pl, k, out_idx, out_score), s);
 }
 
 int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
@@ -560,27 +632,30 @@ int reuse_impl(const idx_problem* p, int32_t k, int32_t G, int32_t* out_idx, flo
 }
 
 GroupBlockPlan plan_group_block(const idx_problem* p, int G, int Bs, int keep, void* ws,
-                                int32_t* out_blocks) {
+                                int32_t* out_blocks, const void* pooled_in = nullptr) {
   GroupBlockPlan g;
   Carver c(ws);
   g.NG = (p->T + G - 1) / G;
   g.NB = (p->N + Bs - 1) / Bs;
   const int C = keep * Bs;
   const size_t qeb = p->q_dtype == IDX_BF16 ? 2 : 4;
-  const size_t keb = p->k_dtype == IDX_BF16 ? 2 : 4;
+  const size_t keb = pooled_dtype(p->k_dtype) == IDX_F32 ? 4 : 2;
   g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
   g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
   g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
-  g.pooled = c.take<uint8_t>((size_t)p->B * g.NB * p->D * keb);
+  g.pooled = pooled_in ? const_cast<void*>(pooled_in) : c.take<uint8_t>((size_t)p->B * g.NB * p->D * keb);
   g.chunkP = chunk_rows(p->B, rstride(g.NB) * 4, g.NG);
   g.cscores = c.take<float>((size_t)p->B * g.chunkP * rstride(g.NB));
   g.blocks = out_blocks ? out_blocks : c.take<int32_t>((size_t)p->B * g.NG * keep);
   g.n_kept = c.take<int32_t>((size_t)p->B * g.NG);
-  g.list = c.take<int32_t>((size_t)p->B * g.NG * C);
-  g.cnt = c.take<int32_t>((size_t)p->B * g.NG);
-  g.chunkG = chunk_rows(p->B, (int64_t)G * rstride(C) * 4, g.NG);
-  const int rows = std::max(std::min(p->T, g.chunkG * G), g.chunkP);
-  g.mscores = c.take<float>((size_t)p->B * std::min(p->T, g.chunkG * G) * rstride(C));
+  g.dec = blocks_by_decode(p, Bs, keep);
+  g.list = g.dec ? nullptr : c.take<int32_t>((size_t)p->B * g.NG * C);
+  g.cnt = g.dec ? nullptr : c.take<int32_t>((size_t)p->B * g.NG);
+  g.chunkG = g.dec ? 1 : chunk_rows(p->B, (int64_t)G * rstride(C) * 4, g.NG);
+  const int rows = g.dec ? g.chunkP : std::max(std::min(p->T, g.chunkG * G), g.chunkP);
+  g.mscores = g.dec ? nullptr : c.take<float>((size_t)p->B * std::min(p->T, g.chunkG * G) * rstride(C));
+  // a pair of queries shares a scan work-group when both are in one group
+  if (g.dec) carve_decode(g.dp, c, p, C, G % 2 == 0 ? 2 : 1);
   g.row_len = c.take<int32_t>((size_t)p->B * rows);
   g.meta = c.take<int32_t>((size_t)p->B * rows * 4);
   g.bytes = c.off + kAlign;
@@ -589,37 +664,51 @@ GroupBlockPlan plan_group_block(const idx_problem* p, int G, int Bs, int keep, v
 
 // Block-filtered group proxy: each group's proxy scores the pooled blocks of its prefix and
 // keeps `keep` of them; every member refines the tokens of the kept blocks.
-int group_block_impl(const idx_problem* p, int32_t k, int32_t G, int32_t Bs, int32_t keep,
-                     int32_t* out_idx, float* out_score, int32_t* out_blocks, void* ws, size_t ws_bytes,
-                     hipStream_t s) {
-  int st = validate(p, k, out_idx, out_score);
-  if (st) return st;
-  if (p->q_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;     // FP8 queries: dense entry points only
-  if (G < 1 || Bs < 1 || keep < 1) return IDX_ERR_INVALID_ARG;
-  if (p->k_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;
+int launch_pool_of(const idx_problem* p, int Bs, int NB, void* pooled, hipStream_t s) {
+  PoolArgs po;
+  po.keys = p->k; po.k_dtype = p->k_dtype; po.k_len = p->k_len; po.k_scale = p->k_scale;
+  po.B = p->B; po.N = p->N; po.D = p->D; po.block_size = Bs; po.n_blocks = NB;
+  po.pooled = pooled;
+  return from_hip(timed("pool", s, [&] { return launch_pool(po, s); }));
+}
+
+int check_block_args(const idx_problem* p, int32_t Bs, int32_t keep, const int32_t* out_blocks,
+                     const void* pooled_in) {
+  if (Bs < 1 || keep < 1) return IDX_ERR_INVALID_ARG;
   if ((p->N + (int64_t)Bs - 1) / Bs > 65536 || keep > 32767) return IDX_ERR_UNSUPPORTED;
   if ((int64_t)keep * Bs > (int64_t)INT32_MAX / 4) return IDX_ERR_UNSUPPORTED;
   if (out_blocks && !aligned(out_blocks, 4)) return IDX_ERR_ALIGN;
-  GroupBlockPlan pl = plan_group_block(p, G, Bs, keep, nullptr, out_blocks);
+  if (pooled_in && !aligned(pooled_in, 16)) return IDX_ERR_ALIGN;
+  return IDX_OK;
+}
+
+// Block-filtered group proxy: each group's proxy scores the pooled blocks of its prefix and
+// keeps `keep` of them; every member refines the tokens of the kept blocks. pooled_in: the
+// caller's pooled cache, or null to pool here.
+int group_block_impl(const idx_problem* p, int32_t k, int32_t G, int32_t Bs, int32_t keep,
+                     int32_t* out_idx, float* out_score, int32_t* out_blocks, const void* pooled_in,
+                     void* ws, size_t ws_bytes, hipStream_t s) {
+  int st = validate(p, k, out_idx, out_score);
+  if (st) return st;
+  if (p->q_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;     // FP8 queries: dense entry points only
+  if (G < 1) return IDX_ERR_INVALID_ARG;
+  if ((st = check_block_args(p, Bs, keep, out_blocks, pooled_in))) return st;
+  GroupBlockPlan pl = plan_group_block(p, G, Bs, keep, nullptr, out_blocks, pooled_in);
   if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
-  pl = plan_group_block(p, G, Bs, keep, align_ws(ws), out_blocks);
+  pl = plan_group_block(p, G, Bs, keep, align_ws(ws), out_blocks, pooled_in);
 
   ProxyArgs pa;
   pa.q = p->q; pa.q_dtype = p->q_dtype; pa.w = p->w; pa.q_pos = p->q_pos;
   pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.D = p->D; pa.G = G; pa.n_groups = pl.NG;
   pa.pq = pl.pq; pa.pw = pl.pw; pa.ppos = pl.ppos;
   if ((st = from_hip(timed("proxy", s, [&] { return launch_proxy(pa, s); })))) return st;
-  PoolArgs po;
-  po.keys = p->k; po.k_dtype = p->k_dtype; po.k_len = p->k_len;
-  po.B = p->B; po.N = p->N; po.D = p->D; po.block_size = Bs; po.n_blocks = pl.NB;
-  po.pooled = pl.pooled;
-  if ((st = from_hip(timed("pool", s, [&] { return launch_pool(po, s); })))) return st;
+  if (!pooled_in && (st = launch_pool_of(p, Bs, pl.NB, pl.pooled, s))) return st;
   // coarse: the proxies against the pooled blocks, block j sits at position j * Bs
   for (int c0 = 0; c0 < pl.NG; c0 += pl.chunkP) {
     const int c1 = std::min(pl.NG, c0 + pl.chunkP);
     ScoreArgs a = base_score_args(p);
     a.q = pl.pq; a.w = pl.pw; a.q_pos = pl.ppos; a.T = pl.NG;
-    a.keys = pl.pooled; a.k_scale = nullptr; a.key_cap = pl.NB;
+    a.keys = pl.pooled; a.k_dtype = pooled_dtype(p->k_dtype); a.k_scale = nullptr; a.key_cap = pl.NB;
     a.pos_stride = Bs; a.count_div = Bs;
     a.c0 = c0; a.c1 = c1;
     a.scores = pl.cscores; a.score_stride = rstride(pl.NB); a.row_len = pl.row_len;
@@ -637,6 +726,8 @@ int group_block_impl(const idx_problem* p, int32_t k, int32_t G, int32_t Bs, int
          return launch_sort_rows(pl.blocks, keep, pl.n_kept, p->B * pl.NG, keep, pl.NB, s);
        }))))
     return st;
+  if (pl.dec)
+    return refine_blocks_decode(p, k, pl.dp, pl.blocks, pl.n_kept, keep, Bs, G, pl.NG, out_idx, out_score, s);
   const int C = keep * Bs;
   if ((st = from_hip(timed("sort", s, [&] {
          return launch_expand_blocks(pl.blocks, pl.n_kept, keep, Bs, p->N, p->k_len, pl.NG, pl.list, pl.cnt,
@@ -684,30 +775,23 @@ int refine_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, const int
 }
 
 int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_t* out_idx,
-               float* out_score, int32_t* out_blocks, void* ws, size_t ws_bytes, hipStream_t s) {
+               float* out_score, int32_t* out_blocks, const void* pooled_in, void* ws, size_t ws_bytes,
+               hipStream_t s) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
   if (p->q_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;     // FP8 queries: dense entry points only
-  if (Bs < 1 || keep < 1) return IDX_ERR_INVALID_ARG;
-  if (p->k_dtype == IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;
-  if ((p->N + (int64_t)Bs - 1) / Bs > 65536 || keep > 32767) return IDX_ERR_UNSUPPORTED;
-  if ((int64_t)keep * Bs > (int64_t)INT32_MAX / 4) return IDX_ERR_UNSUPPORTED;
-  if (out_blocks && !aligned(out_blocks, 4)) return IDX_ERR_ALIGN;
-  BlockPlan pl = plan_block(p, Bs, keep, nullptr, out_blocks);
+  if ((st = check_block_args(p, Bs, keep, out_blocks, pooled_in))) return st;
+  BlockPlan pl = plan_block(p, Bs, keep, nullptr, out_blocks, pooled_in);
   if (!ws || ws_bytes < pl.bytes) return IDX_ERR_WORKSPACE;
-  pl = plan_block(p, Bs, keep, align_ws(ws), out_blocks);
+  pl = plan_block(p, Bs, keep, align_ws(ws), out_blocks, pooled_in);
 
-  PoolArgs po;
-  po.keys = p->k; po.k_dtype = p->k_dtype; po.k_len = p->k_len;
-  po.B = p->B; po.N = p->N; po.D = p->D; po.block_size = Bs; po.n_blocks = pl.NB;
-  po.pooled = pl.pooled;
-  if ((st = from_hip(timed("pool", s, [&] { return launch_pool(po, s); })))) return st;
+  if (!pooled_in && (st = launch_pool_of(p, Bs, pl.NB, pl.pooled, s))) return st;
 
   // coarse: pooled blocks, block j sits at position j * Bs
   for (int c0 = 0; c0 < p->T; c0 += pl.chunkT1) {
     const int c1 = std::min(p->T, c0 + pl.chunkT1);
     ScoreArgs a = base_score_args(p);
-    a.keys = pl.pooled; a.k_scale = nullptr; a.key_cap = pl.NB;
+    a.keys = pl.pooled; a.k_dtype = pooled_dtype(p->k_dtype); a.k_scale = nullptr; a.key_cap = pl.NB;
     a.pos_stride = Bs; a.count_div = Bs;
     a.c0 = c0; a.c1 = c1;
     a.scores = pl.cscores; a.score_stride = rstride(pl.NB); a.row_len = pl.row_len;
@@ -725,6 +809,19 @@ int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_
          return launch_sort_rows(pl.blocks, keep, pl.n_kept, p->B * p->T, keep, pl.NB, s);
        }))))
     return st;
+  if (pl.dec)
+    return refine_blocks_decode(p, k, pl.dp, pl.blocks, pl.n_kept, keep, Bs, 1, p->T, out_idx, out_score, s);
+  const int C = keep * Bs;
+  if (pl.lists) {
+    // each query's kept tokens as its own list (groups of one), refined by the list-mode kernel
+    if ((st = from_hip(timed("sort", s, [&] {
+           return launch_expand_blocks(pl.blocks, pl.n_kept, keep, Bs, p->N, p->k_len, p->T, pl.list, pl.cnt,
+                                       p->B * p->T, s);
+         }))))
+      return st;
+    return refine_lists(p, k, 1, C, C, p->T, pl.chunkT2, pl.list, pl.cnt, pl.rscores, pl.row_len, pl.meta,
+                        out_idx, out_score, s);
+  }
   // token refine inside the kept blocks
   const int qt = score_queries_per_tile(p->H);
   for (int c0 = 0; c0 < p->T; c0 += pl.chunkT2) {
@@ -735,19 +832,31 @@ int block_impl(const idx_problem* p, int32_t k, int32_t Bs, int32_t keep, int32_
     r.B = p->B; r.T = p->T; r.H = p->H; r.D = p->D; r.N = p->N;
     r.blocks = pl.blocks; r.n_kept = pl.n_kept; r.keep_stride = keep; r.block_size = Bs;
     r.t0 = c0; r.t1 = c1;
-    r.scores = pl.rscores; r.score_stride = rstride((int64_t)keep * Bs);
+    r.scores = pl.rscores; r.score_stride = rstride((int64_t)C);
     r.row_len = pl.row_len; r.rows_per_seq = c1 - c0;
     r.row_meta = nullptr; r.topk_k = k;
     r.tiles_per_seq = (c1 - c0 + qt - 1) / qt;
     if ((st = from_hip(timed("block_refine", s, [&] { return launch_block_refine(r, s); }))))
       return st;
-    TopkArgs t = topk_args(pl.rscores, rstride((int64_t)keep * Bs), pl.row_len, p->B * (c1 - c0), k,
+    TopkArgs t = topk_args(pl.rscores, rstride((int64_t)C), pl.row_len, p->B * (c1 - c0), k,
                            c1 - c0, p->T, c0, out_idx, out_score, k);
     t.map_mode = MAP_BLOCKS;
     t.blocks = pl.blocks; t.blocks_stride = keep; t.block_size = Bs;
-    if ((st = from_hip(run_topk(t, keep * Bs, s)))) return st;
+    if ((st = from_hip(run_topk(t, C, s)))) return st;
   }
   return IDX_OK;
+}
+
+// Pooled block keys of the whole cache, for callers that keep them beside the key cache.
+int pool_impl(const idx_problem* p, int32_t Bs, void* pooled, hipStream_t s) {
+  if (!p || p->B <= 0 || p->N <= 0 || p->D <= 0 || !p->k || !pooled || Bs < 1) return IDX_ERR_INVALID_ARG;
+  if (p->k_dtype != IDX_F32 && p->k_dtype != IDX_BF16 && p->k_dtype != IDX_FP8_E4M3) return IDX_ERR_UNSUPPORTED;
+  if (p->k_dtype == IDX_FP8_E4M3 && !p->k_scale) return IDX_ERR_INVALID_ARG;
+  if (!(p->D == 32 || p->D == 64 || p->D == 128)) return IDX_ERR_UNSUPPORTED;
+  if (!aligned(p->k, 16) || !aligned(pooled, 16) || (p->k_len && !aligned(p->k_len, 4)) ||
+      (p->k_scale && !aligned(p->k_scale, 4)))
+    return IDX_ERR_ALIGN;
+  return launch_pool_of(p, Bs, (p->N + Bs - 1) / Bs, pooled, s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -839,7 +948,28 @@ int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
                             int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
                             int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream) {
   try {
-    return block_impl(p, k, block_size, n_blocks_keep, out_idx, out_score, out_blocks, ws,
+    return block_impl(p, k, block_size, n_blocks_keep, out_idx, out_score, out_blocks, nullptr, ws,
+                      ws_bytes, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return IDX_ERR_INTERNAL;
+  }
+}
+
+int idx_block_pool(const idx_problem* p, int32_t block_size, void* pooled, void* stream) {
+  try {
+    return pool_impl(p, block_size, pooled, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return IDX_ERR_INTERNAL;
+  }
+}
+
+int idx_block_coarse_refine_pooled(const idx_problem* p, int32_t k, int32_t block_size,
+                                   int32_t n_blocks_keep, const void* pooled, int32_t* out_idx,
+                                   float* out_score, int32_t* out_blocks, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  try {
+    if (!pooled) return IDX_ERR_INVALID_ARG;
+    return block_impl(p, k, block_size, n_blocks_keep, out_idx, out_score, out_blocks, pooled, ws,
                       ws_bytes, static_cast<hipStream_t>(stream));
   } catch (...) {
     return IDX_ERR_INTERNAL;
@@ -860,8 +990,21 @@ int idx_group_block_refine(const idx_problem* p, int32_t k, int32_t group_size, 
                            int32_t n_blocks_keep, int32_t* out_idx, float* out_score,
                            int32_t* out_blocks, void* ws, size_t ws_bytes, void* stream) {
   try {
-    return group_block_impl(p, k, group_size, block_size, n_blocks_keep, out_idx, out_score, out_blocks, ws,
-                            ws_bytes, static_cast<hipStream_t>(stream));
+    return group_block_impl(p, k, group_size, block_size, n_blocks_keep, out_idx, out_score, out_blocks,
+                            nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return IDX_ERR_INTERNAL;
+  }
+}
+
+int idx_group_block_refine_pooled(const idx_problem* p, int32_t k, int32_t group_size, int32_t block_size,
+                                  int32_t n_blocks_keep, const void* pooled, int32_t* out_idx,
+                                  float* out_score, int32_t* out_blocks, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  try {
+    if (!pooled) return IDX_ERR_INVALID_ARG;
+    return group_block_impl(p, k, group_size, block_size, n_blocks_keep, out_idx, out_score, out_blocks,
+                            pooled, ws, ws_bytes, static_cast<hipStream_t>(stream));
   } catch (...) {
     return IDX_ERR_INTERNAL;
   }

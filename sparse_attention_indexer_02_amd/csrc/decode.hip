@@ -22,8 +22,14 @@
 //     written to the row's candidate list (at the sub-chunk's own slots, with their count). The
 //     row's top-k is inside the union of the sub-chunks' top-k, so every key the selection can
 //     take is a candidate.
+//   With a table of kept blocks (the block filter of "HISA ...", abstract, at decode) the same
+//   scan walks the tokens of a row's kept blocks instead of its whole prefix: slot j of the row
+//   is the j-th kept token (blocks ascending, so slot order is token order), a 16-key block never
+//   straddles two kept blocks (blocks of 16 tokens or more, a power of two), and a query's
+//   visible slots are those of its causal prefix, a prefix of the slots.
 // decode_select_kernel: work-group = row. The top-k of the row's candidates (radix select over
-//   the order-preserving keys, ties to the lowest slots) and the padding.
+//   the order-preserving keys, ties to the lowest slots) and the padding; kept-block slots are
+//   written out as their tokens.
 #include <algorithm>
 #include <type_traits>
 
@@ -59,7 +65,7 @@ __device__ __forceinline__ int frag_d0(int s, int g) {
 }
 
 
-template <int D, int HB, int KST, int PF>
+template <int D, int HB, int KST, int PF, bool BLK>
 __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a) {
   constexpr int NS = D / 32;                      // K=32 MFMA steps
   constexpr int KEB = KST == DT_FP8 ? 1 : 2;      // key bytes per element
@@ -70,24 +76,55 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
   uint32_t* hist = reinterpret_cast<uint32_t*>(lds + 8 * a.sub);   // [2][2048] 16-bit bins
   uint32_t* misc = hist + 2 * 2048;                                // [32]
   uint32_t* sink = misc + 32;                                      // [2][64] per-lane sinks
+  int32_t* btab = reinterpret_cast<int32_t*>(sink + 128);          // BLK: [keep_stride] kept blocks
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int b = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
-  const int t0 = 2 * blockIdx.y;
-  const bool two = t0 + 1 < a.T;
+  const int t0 = a.pair * blockIdx.y;
+  const bool two = a.pair == 2 && t0 + 1 < a.T;
   const int nrows = two ? 2 : 1;
   const int kl = a.k_len ? max(0, min(a.k_len[b], a.N)) : a.N;
   const int64_t r0 = (int64_t)b * a.T + t0, r1 = two ? r0 + 1 : r0;
   const int p0 = a.q_pos[r0], p1 = a.q_pos[r1];
   const int P0 = p0 < 0 ? 0 : min(p0 + 1, kl), P1 = p1 < 0 ? 0 : min(p1 + 1, kl);
+  // visible slots of each query: its prefix, or with kept blocks the kept tokens inside it
+  int V0 = P0, V1 = P1, vmax = kl;
+  if constexpr (BLK) {
+    const int64_t lrow = (int64_t)b * a.n_groups + t0 / a.group_size;
+    const int nk = max(0, min(a.n_kept[lrow], a.keep_stride));
+    const int bsz = 1 << a.blk_shift;
+    uint32_t s0 = 0, s1 = 0;
+    for (int j = tid; j < nk; j += DC_THREADS) {
+      const int blk = a.blocks[lrow * a.keep_stride + j];
+      btab[j] = blk;
+      const int base = blk << a.blk_shift;
+      s0 += (uint32_t)min(max(P0 - base, 0), bsz);
+      s1 += (uint32_t)min(max(P1 - base, 0), bsz);
+    }
+    s0 = wave_bcast(wave_scan_dpp(s0), 63);
+    s1 = wave_bcast(wave_scan_dpp(s1), 63);
+    if (lane == 0) {
+      misc[wave] = s0;
+      misc[8 + wave] = s1;
+    }
+    __syncthreads();
+    V0 = V1 = 0;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) {
+      V0 += (int)misc[w];
+      V1 += (int)misc[8 + w];
+    }
+    vmax = nk << a.blk_shift;
+    __syncthreads();
+  }
   const int c0 = chunk * a.chunk;
-  const int c1 = min(c0 + a.chunk, max(P0, P1));
+  const int c1 = min(c0 + a.chunk, max(V0, V1));
   {
     // sub-chunks of this chunk past the causal limit have no candidates
     const int s_lo = c0 >= c1 ? c0 / a.sub : (c1 + a.sub - 1) / a.sub;
-    const int s_hi = min(c0 + a.chunk, a.N);
+    const int s_hi = min(c0 + a.chunk, a.vn);
     for (int sg = s_lo + tid; sg * a.sub < s_hi; sg += DC_THREADS) {
       a.ccount[r0 * a.nsegs + sg] = 0u;
       if (two) a.ccount[r1 * a.nsegs + sg] = 0u;
@@ -156,20 +193,30 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     // ever copied (a copy would wait for the load)
     u32x4_t raw[PF][NLD];
     float scl[PF];
+    // token of lane n's key in block i (clamped: always issued; with kept blocks, slot -> token
+    // through the LDS table, the same entry for a whole 16-key block)
     auto key_of = [&](int i) {
-      const int blk = min(i * DC_WAVES + wave, nblk - 1);           // clamped: always issued
-      return min(sub0 + blk * DC_KB + n, kl - 1);
+      const int blk = min(i * DC_WAVES + wave, nblk - 1);
+      int v = sub0 + blk * DC_KB + n;
+      if constexpr (BLK) {
+        v = min(v, vmax - 1);
+        v = max((btab[v >> a.blk_shift] << a.blk_shift) | (v & ((1 << a.blk_shift) - 1)), 0);
+      }
+      return min(v, kl - 1);
     };
-    auto issue_keys = [&](int i, u32x4_t (&dst)[NLD]) {
-      const uint32_t off = (uint32_t)key_of(i) * (D * KEB) + lane_koff;
+    auto issue_keys_at = [&](int tok, u32x4_t (&dst)[NLD]) {
+      const uint32_t off = (uint32_t)tok * (D * KEB) + lane_koff;
 #pragma unroll
       for (int j = 0; j < NLD; ++j)
         dst[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kseq + off + 64 * j));
     };
-    auto issue_scale = [&](int i, float& sc) {
-      if constexpr (KST == DT_FP8) sc = *reinterpret_cast<const float*>(sseq + (uint32_t)key_of(i) * 4u);
+    auto issue_scale_at = [&](int tok, float& sc) {
+      if constexpr (KST == DT_FP8) sc = *reinterpret_cast<const float*>(sseq + (uint32_t)tok * 4u);
       else sc = 1.f;
     };
+    // with kept blocks, slot u's token is kept from the issue of its keys to that of its scale
+    // (the table read happens at the top of the slot, well before the issue)
+    int ktok[PF];
     // the previous sub-chunk's candidate stores are complete here, so that the block loop
     // below only ever waits for its own, in-order loads; the prologue issues in the loop's
     // order (slot u: keys of its block, then the scale of the previous slot's block)
@@ -177,8 +224,10 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int up = (u + PF - 1) % PF;
-      issue_keys(u, raw[u]);
-      issue_scale(up, scl[up]);
+      ktok[u] = key_of(u);
+      issue_keys_at(ktok[u], raw[u]);
+      if constexpr (BLK) issue_scale_at(ktok[u == 0 ? 0 : up], scl[up]);
+      else issue_scale_at(key_of(up), scl[up]);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -258,6 +307,8 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
         const int i = i0 + u;
         const int x = u & 1;
         const int up = (u + PF - 1) % PF;                            // slot of block i - 1
+        int ntok = 0;
+        if constexpr (BLK) ntok = key_of(i + PF);
         bf16x8_t bfr[NS];
         bfr[0] = convert(raw[u], 0);
         Epi st;
@@ -270,12 +321,20 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
           const int s = t / (2 * HB), hb = (t >> 1) % HB, q = t & 1;
           acc[x][q][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[q][hb][s], bfr[s], s == 0 ? f32x4v_t{} : acc[x][q][hb], 0, 0, 0);
           if (t % (2 * HB) == 0 && s + 1 < NS) bfr[s + 1] = convert(raw[u], s + 1);
-          if (t == (NS - 2) * 2 * HB) issue_keys(i + PF, raw[u]);
+          if (t == (NS - 2) * 2 * HB) {
+            if constexpr (BLK) {
+              ktok[u] = ntok;
+              issue_keys_at(ntok, raw[u]);
+            } else {
+              issue_keys_at(key_of(i + PF), raw[u]);
+            }
+          }
 #pragma unroll
           for (int k = t * NPIECE / NM; k < (t + 1) * NPIECE / NM; ++k) piece(k, st, i - 1, acc[x ^ 1], scl[up]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        issue_scale(i - 1 + PF, scl[up]);
+        if constexpr (BLK) issue_scale_at(ktok[up], scl[up]);
+        else issue_scale_at(key_of(i - 1 + PF), scl[up]);
       }
     }
     epilogue(iters - 1, acc[1], scl[PF - 1]);                      // iters is a multiple of even PF
@@ -286,7 +345,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       if (qq < nrows) {
-        const int lim = min(sub1, qq ? P1 : P0) - sub0;               // visible slots
+        const int lim = min(sub1, qq ? V1 : V0) - sub0;               // visible slots
         uint32_t* hq = hist + qq * 2048;
         for (int j = 4 * tid; j < lim; j += 4 * DC_THREADS) {
           const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ssc + qq * a.sub + j);
@@ -377,7 +436,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     auto sel_flags = [&](int qq, int st, uint32_t thr, uint32_t (&key)[4], bool (&f)[4]) {
       const int j0 = st * 4 * DC_THREADS + wave * 256 + 4 * lane;
       const int jr = min(j0, a.sub - 4);
-      const int lim = min(len, (qq ? P1 : P0) - sub0);
+      const int lim = min(len, (qq ? V1 : V0) - sub0);
       const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ssc + qq * a.sub + jr);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -515,6 +574,14 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
   uint32_t* g2p = a.cand2_idx + r * a.cand_cap;
   int32_t* oidx = a.out_idx + r * a.k;
   float* osc = a.out_score ? a.out_score + r * a.k : nullptr;
+  // slot -> token (kept-block slots through the row's table; the selected slots are visible, so
+  // inside the kept blocks)
+  const int32_t* tab = a.blocks ? a.blocks + ((r / a.T) * a.n_groups + (r % a.T) / a.group_size) * a.keep_stride
+                                : nullptr;
+  auto tok = [&](uint32_t sl) -> int32_t {
+    if (!tab) return (int32_t)sl;
+    return (tab[sl >> a.blk_shift] << a.blk_shift) | (int32_t)(sl & ((1u << a.blk_shift) - 1u));
+  };
 
   // ---- candidate count M
   uint32_t M = 0;
@@ -703,7 +770,7 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
       const uint32_t sl = ir[u];
       if (sel) {
         const uint32_t pos = ps + __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms, 0u));
-        oidx[pos] = (int32_t)sl;
+        oidx[pos] = tok(sl);
         if (osc) osc[pos] = key2f(xr[u]);
       }
       if (cand) {
@@ -743,7 +810,7 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
         const uint32_t bs = __builtin_amdgcn_mbcnt_hi((uint32_t)(ms[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ms[u], 0u));
         const uint32_t bq = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mc[u], 0u));
         if ((ms[u] >> lane) & 1u) {
-          oidx[ps + bs] = (int32_t)bt.i[u];
+          oidx[ps + bs] = tok(bt.i[u]);
           if (osc) osc[ps + bs] = key2f(bt.x[u]);
         }
         if ((mc[u] >> lane) & 1u) {
@@ -840,7 +907,7 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
       pb = wave_bcast(pb, 0);
       if (sel) {
         const uint32_t pos = pb + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        oidx[pos] = (int32_t)i;
+        oidx[pos] = tok(i);
         if (osc) osc[pos] = key2f(x);
       }
     }
@@ -858,17 +925,25 @@ bool decode_supported(int q_dtype, int k_dtype, int H, int D, int T, int N) {
          (D == 64 || D == 128) && T <= 4 && N >= 2048 && seq_bytes < (int64_t(1) << 31);
 }
 
-size_t decode_scan_lds(int sub) { return (size_t)8 * sub + 2 * 2048 * 4 + (32 + 128) * 4; }
+bool decode_blocks_supported(int q_dtype, int k_dtype, int H, int D, int T, int N, int block_size, int keep) {
+  return decode_supported(q_dtype, k_dtype, H, D, T, N) && block_size >= DC_KB &&
+         (block_size & (block_size - 1)) == 0 && keep <= DECODE_KEEP_MAX;
+}
+
+size_t decode_scan_lds(int sub, int keep) {
+  return (size_t)8 * sub + 2 * 2048 * 4 + (32 + 128) * 4 + (size_t)4 * keep;
+}
 
 template <int D, int HB, int KST>
 static hipError_t launch_scan(const DecodeArgs& a, hipStream_t s) {
-  auto kfn = decode_scan_kernel<D, HB, KST, dc_pf<KST>()>;
+  const bool blk = a.blocks != nullptr;
+  auto kfn = blk ? decode_scan_kernel<D, HB, KST, dc_pf<KST>(), true> : decode_scan_kernel<D, HB, KST, dc_pf<KST>(), false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)decode_scan_lds(DC_SUB));
+                                     (int)decode_scan_lds(DC_SUB, blk ? DECODE_KEEP_MAX : 0));
   if (e != hipSuccess) return e;
-  dim3 grid(a.B * a.nchunk, (a.T + 1) / 2);
-  hipLaunchKernelGGL(kfn, grid, dim3(DC_THREADS), decode_scan_lds(a.sub), s, a);
+  dim3 grid(a.B * a.nchunk, (a.T + a.pair - 1) / a.pair);
+  hipLaunchKernelGGL(kfn, grid, dim3(DC_THREADS), decode_scan_lds(a.sub, blk ? a.keep_stride : 0), s, a);
   return hipGetLastError();
 }
 
@@ -882,6 +957,10 @@ static hipError_t launch_scan_h(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_scan(const DecodeArgs& a, hipStream_t s) {
   if (a.sub < DC_KB || a.sub > DC_SUB || a.sub % 64) return hipErrorInvalidValue;
+  if (a.pair != 1 && a.pair != 2) return hipErrorInvalidValue;
+  if (a.blocks && (a.keep_stride < 1 || a.keep_stride > DECODE_KEEP_MAX || a.blk_shift < 4 ||
+                   a.group_size < 1 || (a.pair == 2 && a.group_size % 2) || !a.n_kept))
+    return hipErrorInvalidValue;
   if (a.k_dtype == DT_FP8)
     return a.D == 128 ? launch_scan_h<128, DT_FP8>(a, s) : launch_scan_h<64, DT_FP8>(a, s);
   return a.D == 128 ? launch_scan_h<128, DT_BF16>(a, s) : launch_scan_h<64, DT_BF16>(a, s);

@@ -80,8 +80,9 @@ struct ReuseArgs {
 
 struct PoolArgs {
   const void* keys; int k_dtype; const int32_t* k_len;
+  const float* k_scale;                  // [B, N] for FP8 keys
   int B, N, D, block_size, n_blocks;    // n_blocks = ceil(N / block_size) (row capacity)
-  void* pooled;                          // [B, n_blocks, D] in the key format
+  void* pooled;                          // [B, n_blocks, D]: fp32 for fp32 keys, else bf16
 };
 
 struct BlockRefineArgs {
@@ -116,7 +117,16 @@ struct DecodeArgs {
   int cand_cap;                    // >= N, multiple of 64
   int k;                           // selection size
   int32_t* out_idx; float* out_score;                        // [B, T, k]
+  int pair;                        // queries per scan work-group: 2, or 1 where a pair would span
+                                   // two kept-block lists
+  int vn;                          // slots per row: N, or keep_stride << blk_shift with blocks
+  // kept-block mode (blocks != NULL): the slots of row b*T+t are the tokens of the kept blocks of
+  // list row b*n_groups + t/group_size, ascending: slot j is token
+  // (blocks[row][j >> blk_shift] << blk_shift) + (j & (2^blk_shift - 1)); n_kept[row] blocks
+  const int32_t* blocks; const int32_t* n_kept;
+  int keep_stride, blk_shift, group_size, n_groups;
 };
+constexpr int DECODE_KEEP_MAX = 2048;  // kept blocks per list in the kept-block scan (LDS table)
 
 hipError_t launch_score(const ScoreArgs& a, int n_splits, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s);
@@ -136,6 +146,8 @@ hipError_t launch_sort_rows(int32_t* rows, int stride, const int32_t* count, int
                             int max_value, hipStream_t s);
 bool score_supported(int q_dtype, int k_dtype, int H, int D);
 bool decode_supported(int q_dtype, int k_dtype, int H, int D, int T, int N);
+// the kept-block scan: 2^blk_shift-token blocks with blk_shift >= 4, at most DECODE_KEEP_MAX kept
+bool decode_blocks_supported(int q_dtype, int k_dtype, int H, int D, int T, int N, int block_size, int keep);
 hipError_t launch_decode_scan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t s);
 

@@ -132,8 +132,40 @@ hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// FP8 keys: the same ascending sum over the fp32 key values decode(byte) * scale (one rounding
+// each; multiply and add kept apart: the compiler would otherwise contract them into an FMA,
+// which rounds once).
+__device__ __forceinline__ void sum_rows8_fp8(const uint8_t* base, const float* scale, int64_t e0, int64_t step,
+                                              int r0, int r1, float (&s)[8]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0.f;
+  int r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    u32x2_t v[4];
+    float sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = *reinterpret_cast<const u32x2_t*>(base + e0 + (int64_t)(r + u) * step);
+      sc[u] = scale[r + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        s[i] = s[i] + e4m3_to_f32((v[u][i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc[u];
+  }
+  for (; r < r1; ++r) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(base + e0 + (int64_t)r * step);
+    const float sc = scale[r];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      s[i] = s[i] + e4m3_to_f32((v[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc;
+  }
+}
+
 // Thread = 8 dimensions of one pooled block; D / 8 threads per block, 256 / (D / 8) blocks per
-// work-group.
+// work-group. DT is the key format; pooled keys are fp32 for fp32 keys, bf16 otherwise.
 template <int DT>
 __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   const int tpb = a.D / 8;
@@ -150,19 +182,24 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
     for (int i = 0; i < 8; ++i) m[i] = 0.f;
   } else {
     float s[8];
-    sum_rows8<DT>(a.keys, (int64_t)b * a.N * a.D + d, a.D, s0, s1, s);
+    if constexpr (DT == DT_FP8)
+      sum_rows8_fp8(reinterpret_cast<const uint8_t*>(a.keys), a.k_scale + (int64_t)b * a.N,
+                    (int64_t)b * a.N * a.D + d, a.D, s0, s1, s);
+    else
+      sum_rows8<DT>(a.keys, (int64_t)b * a.N * a.D + d, a.D, s0, s1, s);
     const float n = (float)(s1 - s0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) m[i] = __fdiv_rn(s[i], n);
   }
-  store8<DT>(a.pooled, o, m);
+  store8<DT == DT_F32 ? DT_F32 : DT_BF16>(a.pooled, o, m);
 }
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
   const int per_wg = 256 / (a.D / 8);
   const int64_t nb = (int64_t)a.B * a.n_blocks;
   dim3 grid((unsigned)((nb + per_wg - 1) / per_wg));
-  if (a.k_dtype == DT_BF16) hipLaunchKernelGGL(pool_kernel<DT_BF16>, grid, dim3(256), 0, s, a);
+  if (a.k_dtype == DT_FP8) hipLaunchKernelGGL(pool_kernel<DT_FP8>, grid, dim3(256), 0, s, a);
+  else if (a.k_dtype == DT_BF16) hipLaunchKernelGGL(pool_kernel<DT_BF16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(pool_kernel<DT_F32>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

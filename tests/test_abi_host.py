@@ -126,8 +126,22 @@ def test_variant_arguments(L):
                                                          None, None, 0x60000, 1 << 40, None)
     assert b(0, 4) == -1 and b(16, 0) == -1
     assert b(16, 40000) == -2
-    fp8 = _problem(k_dtype=idx.FP8_E4M3, k_scale=0x70000)
-    assert b(16, 4, fp8) == -2
+    assert b(16, 4, _problem(k_dtype=idx.FP8_E4M3)) == -1           # fp8 keys need k_scale
+
+
+def test_pooled_arguments(L):
+    p = _problem()
+    bp = lambda Bs, pooled, pp=p: L.idx_block_pool(ctypes.byref(pp), Bs, pooled, None)
+    assert bp(16, None) == -1 and bp(0, 0x70000) == -1
+    assert bp(16, 0x70008) == -3                                     # pooled not 16-byte aligned
+    assert bp(16, 0x70000, pp=_problem(D=48)) == -2
+    assert bp(16, 0x70000, pp=_problem(k_dtype=idx.FP8_E4M3)) == -1  # fp8 keys need k_scale
+    bc = lambda pooled, ws_bytes=1 << 40: L.idx_block_coarse_refine_pooled(
+        ctypes.byref(p), 8, 16, 4, pooled, 0x50000, None, None, 0x60000, ws_bytes, None)
+    assert bc(None) == -1 and bc(0x70008) == -3 and bc(0x70000, ws_bytes=100) == -4
+    gc = lambda pooled, ws_bytes=1 << 40: L.idx_group_block_refine_pooled(
+        ctypes.byref(p), 8, 4, 16, 4, pooled, 0x50000, None, None, 0x60000, ws_bytes, None)
+    assert gc(None) == -1 and gc(0x70008) == -3 and gc(0x70000, ws_bytes=100) == -4
 
 
 def test_refine_given_arguments(L):
@@ -157,7 +171,7 @@ def test_group_block_arguments(L):
         ctypes.byref(pp), 8, G, Bs, keep, 0x50000, None, None, 0x60000, ws_bytes, None)
     assert gb(0, 16, 4) == -1 and gb(4, 0, 4) == -1 and gb(4, 16, 0) == -1
     assert gb(4, 16, 40000) == -2
-    assert gb(4, 16, 4, pp=_problem(k_dtype=idx.FP8_E4M3, k_scale=0x70000)) == -2
+    assert gb(4, 16, 4, pp=_problem(k_dtype=idx.FP8_E4M3)) == -1     # fp8 keys need k_scale
     assert gb(4, 16, 4, ws_bytes=100) == -4
     assert L.idx_group_block_workspace_bytes(ctypes.byref(p), 8, 4, 16, 4) > 0
     assert L.idx_group_block_workspace_bytes(ctypes.byref(p), 8, 0, 16, 4) == 0

@@ -11,6 +11,7 @@ import workloads as W
 import sparse_attention_indexer_02_amd as idx
 from gpu_util import dev, say
 from parity import check_selection
+from block_checks import check_gb
 
 pytestmark = pytest.mark.gpu
 
@@ -22,24 +23,6 @@ def run_gb(prob, k, G, Bs, keep):
                                           return_blocks=True)
     torch.cuda.synchronize()
     return oi.cpu().numpy(), osc.cpu().numpy(), blk.cpu().numpy()
-
-
-def check_gb(prob, k, G, Bs, keep, gi, gs, gb, groups, name):
-    inp = oracle.Inputs(prob)
-    pooled = {b: oracle.pool_keys(prob, b, Bs) for b in {b for b, _ in groups}}
-    for b, g in groups:
-        sc = oracle.group_block_scan(inp, b, g, G, Bs, keep, pooled[b])
-        n_elig = len(sc["block_scores"])
-        check_selection(gb[b, g], None, np.arange(n_elig), sc["block_scores"], sc["block_magnitude"],
-                        keep, prob.D, ctx=f"{name} blocks b{b} g{g}", oracle_sel=sc["blocks"])
-        kept = gb[b, g][gb[b, g] >= 0].astype(np.int64)
-        assert (np.diff(kept) > 0).all()
-        toks = (kept[:, None] * Bs + np.arange(Bs)[None]).reshape(-1)
-        for t in oracle.group_members(prob.T, G, g):
-            # the oracle's token scores over the GPU's own kept blocks (inside the prefix)
-            r = oracle.refine_row(inp, b, t, k, toks)
-            check_selection(gi[b, t], gs[b, t], r["universe"], r["all_scores"], r["magnitude"], k,
-                            prob.D, ctx=f"{name} b{b} t{t}")
 
 
 def test_group_block_small_ragged_batch():

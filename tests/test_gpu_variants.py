@@ -12,6 +12,7 @@ import workloads as W
 import sparse_attention_indexer_02_amd as idx
 from gpu_util import dev, say
 from parity import check_selection
+from block_checks import check_block
 
 pytestmark = pytest.mark.gpu
 
@@ -127,31 +128,6 @@ def run_block(prob, k, Bs, keep):
                                            k_len=t["k_len"], return_blocks=True)
     torch.cuda.synchronize()
     return oi.cpu().numpy(), osc.cpu().numpy(), blk.cpu().numpy()
-
-
-def check_block(prob, k, Bs, keep, gi, gs, gb, rows, name):
-    inp = oracle.Inputs(prob)
-    pooled = {}
-    e2e_diff = e2e_tot = 0
-    for b, t in rows:
-        if b not in pooled:
-            pooled[b] = oracle.pool_keys(prob, b, Bs)
-        r = oracle.block_row(inp, b, t, k, Bs, keep, pooled[b])
-        n_elig = len(r["block_scores"])
-        check_selection(gb[b, t], None, np.arange(n_elig), r["block_scores"],
-                        r["block_magnitude"], keep, prob.D, ctx=f"{name} blocks b{b} t{t}",
-                        oracle_sel=r["blocks"])
-        kept = gb[b, t, :min(keep, n_elig)].astype(np.int64)
-        assert (np.diff(kept) > 0).all() and (gb[b, t, min(keep, n_elig):] == -1).all()
-        d = oracle.dense_row(inp, b, t, k)
-        toks = np.sort((kept[:, None] * Bs + np.arange(Bs)[None]).reshape(-1))
-        toks = toks[toks < inp.P(b, t)]
-        check_selection(gi[b, t], gs[b, t], toks, d["all_scores"][toks], d["magnitude"][toks],
-                        k, prob.D, ctx=f"{name} b{b} t{t}")
-        sel = gi[b, t][gi[b, t] >= 0]
-        e2e_diff += len(np.setxor1d(sel, r["ids"])) // 2
-        e2e_tot += len(r["ids"])
-    say(f"{name}: end-to-end differences vs oracle {e2e_diff}/{e2e_tot}")
 
 
 def test_block_small_all_rows():

@@ -171,15 +171,20 @@ def make_tiny(seed=0, L=1024, H=4, D=32, n_heavy=16) -> Problem:
 
 
 def make_decode(B, N, T=2, H=64, D=128, *, seed=0, k_dtype=FP8_E4M3, heavy_frac=0.01,
-                heavy_factor=3.0, w_scale=0.125, k_len=None) -> Problem:
+                heavy_factor=3.0, w_scale=0.125, k_len=None, n_regions=0, region=128) -> Problem:
     """B sequences with N cached keys; the T multi-token-prediction queries of one decode step
-    sit at positions k_len-T .. k_len-1 (each sees the earlier ones' keys)."""
+    sit at positions k_len-T .. k_len-1 (each sees the earlier ones' keys). Heavy keys are single
+    rows (a fraction heavy_frac of the cache), or with n_regions > 0 that many runs of `region`
+    consecutive tokens per sequence (the locality a block-level filter relies on)."""
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, T, H, D), dtype=np.float32)
     keys = np.empty((B, N, D), np.float32)
     for b in range(B):
         keys[b] = rng.standard_normal((N, D), dtype=np.float32)
-    _heavy_rows(rng, keys, heavy_frac, heavy_factor)
+    if n_regions > 0:
+        _heavy_regions(rng, keys, n_regions, region, heavy_factor)
+    else:
+        _heavy_rows(rng, keys, heavy_frac, heavy_factor)
     w = (rng.random((B, T, H), dtype=np.float32) * np.float32(w_scale)).astype(np.float32)
     qs, _ = _store(q, BF16)
     ks, sc = _store(keys, k_dtype)
@@ -222,7 +227,7 @@ def make_banks(prob: Problem, G: int, C: int, seed: int = 0) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------------
-# named workloads (the five shapes the indexer pages' long-context experiments suggest)
+# named workloads (shapes of the long-context prefill and decode settings the indexer pages study)
 
 WORKLOADS = {
     "tiny": dict(op="dense", k=64, gen=lambda seed=0: make_tiny(seed)),
@@ -248,4 +253,11 @@ WORKLOADS = {
                        gen=lambda seed=0: make_hier(131072, 4096, seed=seed)),
     "hier128k": dict(op="block", k=2048, block_size=128, n_blocks_keep=128,
                      gen=lambda seed=0: make_hier(131072, 4096, seed=seed)),
+    # decode with a block filter on the FP8 cache: 32 sequences of 131072 tokens, 2 queries each,
+    # pooled block keys kept beside the cache; per query (block) or shared by a step's 2 queries
+    "decodeblk128k": dict(op="block", k=2048, block_size=128, n_blocks_keep=128, pooled=True,
+                          gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed, n_regions=64)),
+    "decodegblk128k": dict(op="gblock", k=2048, group_size=2, block_size=128, n_blocks_keep=128,
+                           pooled=True,
+                           gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed, n_regions=64)),
 }
