@@ -23,13 +23,19 @@ Sources (web pages, cited by title and section):
   [HISA]  "HISA: Efficient Hierarchical Indexing for Fine-Grained Sparse Attention", abstract:
           blocks of keys are pooled and scored to drop unpromising regions, then the unchanged
           token-level indexer runs only over the tokens of the blocks that were kept.
+  [LatentIndex] "LatentIndex: Cross-Layer Sharing with Layer-Specific Selection for Sparse
+          Attention", abstract: a group of layers shares one latent cache, and each layer scores
+          it directly by absorbing its key decoder into its queries instead of rebuilding its
+          own keys.
 
 Parity status: every function below is pinned by tests/test_oracle_*.py (hand-computed cases,
-library special cases, invariants and reductions). Recall of the group and block variants
+library special cases, invariants, reductions and, for the absorbed queries, the identity with
+scoring rebuilt keys). Recall of the group and block variants
 against the dense indexer has no published value and is reported, not pinned.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from typing import Dict, List, Optional, Tuple
 
@@ -69,6 +75,17 @@ def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:
     nan = (u & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
     r = np.where(nan, (u >> np.uint64(16)) | np.uint64(0x40), r)
     return r.astype(np.uint16)
+
+
+def f64_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """Round binary64 straight to bfloat16 (8 significant bits), nearest-even, in one step (no
+    intermediate fp32 rounding). Finite inputs within bf16's range; subnormals keep the fixed
+    2^-133 spacing."""
+    x = np.asarray(x, np.float64)
+    _, e = np.frexp(x)                                 # |x| = m * 2^e, 0.5 <= m < 1
+    ue = np.maximum(e - 8, -133).astype(np.float64)    # exponent of the bf16 unit in the last place
+    r = np.rint(np.ldexp(x, (-ue).astype(np.int32))) * np.exp2(ue)   # rint: ties to even
+    return f32_to_bf16_bits_rne(r.astype(np.float32))  # r is exact in bf16, so this is a re-encoding
 
 
 def queries_f64(q: np.ndarray, q_dtype: int, q_scale: Optional[np.ndarray] = None) -> np.ndarray:
@@ -420,3 +437,45 @@ def block(prob, k: int, block_size: int, n_keep: int):
             out_sc[b, t, :n] = r["scores"]
             out_blk[b, t, :len(r["blocks"])] = r["blocks"]
     return out_idx, out_sc, out_blk
+
+
+# ----------------------------------------------------------------------------------------------
+# absorbed-query scoring of a shared latent cache  [LatentIndex]
+
+def absorb_queries(q: np.ndarray, q_dtype: int, wk: np.ndarray) -> Dict[str, np.ndarray]:
+    """[LatentIndex] Reading: a layer's indexer key is a linear decoding of the shared latent
+    row, k[s] = c[s] @ Wk (latent c[s] of Dc elements, decoder Wk [Dc, D] in bf16), so
+    q[h] . k[s] = (Wk @ q[h]) . c[s]: the decoder moves into the query, which then scores the
+    latent cache with the unchanged indexer. The absorbed query is itself an indexer query and is
+    stored in the query format, bf16 rounded to nearest-even from its exact value (the reading
+    the proxy query follows).
+
+    q [..., H, D] in q_dtype storage, wk [Dc, D] bf16 bits. Returns dict(
+      bits  [..., H, Dc] uint16: the absorbed queries,
+      exact [..., H, Dc] float64: Wk @ q before rounding,
+      bound [..., H, Dc] float64: D * 2^-24 * sum_d |Wk[j,d] q[h,d]|, the a-priori error of an
+            fp32 evaluation of the same sums, within which another rounding decision is valid)."""
+    q64 = queries_f64(q, q_dtype)
+    w64 = bf16_bits_to_f64(wk)
+    exact = q64 @ w64.T
+    bound = (np.abs(q64) @ np.abs(w64).T) * (q64.shape[-1] * 2.0 ** -24)
+    return dict(bits=f64_to_bf16_bits_rne(exact), exact=exact, bound=bound)
+
+
+def latent_problem(prob, q_lat_bits: np.ndarray):
+    """The indexer problem the absorbed queries pose: the same head weights, positions and cache
+    lengths, queries q_lat (bf16 [B,T,H,Dc]) against the latent cache prob.k [B,N,Dc]."""
+    return dataclasses.replace(prob, q=q_lat_bits, q_dtype=BF16, q_scale=None, wk=None)
+
+
+def latent_definition_row(prob, b: int, t: int, k: int):
+    """One query scored as the layer's own indexer would score it: its original queries against
+    keys rebuilt from the latent cache (k[s] = c[s] @ Wk, exact in float64) over its causal
+    prefix; the top-k as in dense_row. Returns dict(ids, scores, all_scores)."""
+    qp = visible_len(int(prob.q_pos[b, t]), int(prob.k_len[b]))
+    q64 = queries_f64(prob.q[b, t], prob.q_dtype)
+    c64 = keys_f64(prob.k[b, :qp], prob.k_dtype, None if prob.k_scale is None else prob.k_scale[b, :qp])
+    keys = c64 @ bf16_bits_to_f64(prob.wk)
+    sc = index_scores(q64, np.asarray(prob.w[b, t], np.float32).astype(np.float64), keys)
+    ids, top = select_topk(sc, np.arange(qp, dtype=np.int64), k)
+    return dict(ids=ids, scores=top, all_scores=sc)

@@ -38,6 +38,8 @@ class Problem:
     q_pos  [B,T]      int32: key s is visible to query (b,t) iff s <= q_pos[b,t] and s < k_len[b]
     k_len  [B]        int32 valid keys per sequence
     q_scale[B,T,H]    float32, only for FP8_E4M3 queries (real query = decoded byte * scale)
+    wk     [Dc,D]     uint16 bf16 bits, only for a shared latent cache: k then holds latent rows
+                      [B,N,Dc] and a layer's key is latent @ wk (its key decoder)
     """
     q: np.ndarray
     q_dtype: int
@@ -48,6 +50,7 @@ class Problem:
     q_pos: np.ndarray
     k_len: np.ndarray
     q_scale: Optional[np.ndarray] = None
+    wk: Optional[np.ndarray] = None
 
     @property
     def B(self): return self.q.shape[0]
@@ -208,6 +211,34 @@ def make_hier(N, T, H=64, D=128, *, seed=0, rho=0.9, n_regions=64, region=128,
     return Problem(qs, BF16, ks, BF16, None, w, q_pos, np.array([N], np.int32))
 
 
+def make_latent(B, T, N, H=64, D=128, Dc=64, *, seed=0, rho=0.9, k_dtype=BF16, heavy_frac=0.01,
+                heavy_factor=3.0, w_scale=0.125, decode=False) -> Problem:
+    """A layer that scores a shared latent cache: queries of head dimension D, latent rows of Dc
+    elements (N(0,1) with heavy rows, like the key caches), head weights, and the layer's key
+    decoder wk [Dc, D] ~ N(0, 1/Dc) (a random projection: the rebuilt keys latent @ wk have unit
+    variance, no trained weights). Prefill (decode=False): T = N queries at positions 0..N-1 with
+    AR(1) queries; decode: T multi-token-prediction queries at N-T .. N-1 with N(0,1) queries."""
+    rng = np.random.default_rng(seed)
+    if decode:
+        q = rng.standard_normal((B, T, H, D), dtype=np.float32)
+    else:
+        q = _ar1(rng, B, T, (H, D), rho)
+    lat = np.empty((B, N, Dc), np.float32)
+    for b in range(B):
+        lat[b] = rng.standard_normal((N, Dc), dtype=np.float32)
+    _heavy_rows(rng, lat, heavy_frac, heavy_factor)
+    w = (rng.random((B, T, H), dtype=np.float32) * np.float32(w_scale)).astype(np.float32)
+    wk = (rng.standard_normal((Dc, D), dtype=np.float32) / np.float32(np.sqrt(Dc))).astype(np.float32)
+    qs, _ = _store(q, BF16)
+    ks, sc = _store(lat, k_dtype)
+    k_len = np.full(B, N, np.int32)
+    if decode:
+        q_pos = np.broadcast_to((N - T + np.arange(T, dtype=np.int32))[None], (B, T)).astype(np.int32).copy()
+    else:
+        q_pos = np.broadcast_to(np.arange(T, dtype=np.int32), (B, T)).copy()
+    return Problem(qs, BF16, ks, k_dtype, sc, w, q_pos, k_len, wk=f32_to_bf16_bits(wk))
+
+
 def make_banks(prob: Problem, G: int, C: int, seed: int = 0) -> np.ndarray:
     """Candidate token banks for a per-query refine over caller-supplied sets: for each group of
     G consecutive queries, C distinct tokens drawn uniformly from the group's prefix (the tokens
@@ -260,4 +291,11 @@ WORKLOADS = {
     "decodegblk128k": dict(op="gblock", k=2048, group_size=2, block_size=128, n_blocks_keep=128,
                            pooled=True,
                            gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed, n_regions=64)),
+    # a layer scoring a shared 64-dimensional latent cache through absorbed queries (D = 128):
+    # a 64K prefill (bf16 latent) and a 128K decode step (FP8 latent with per-token scales)
+    "latent64k": dict(op="latent", k=2048,
+                      gen=lambda seed=0: make_latent(1, 65536, 65536, seed=seed, rho=0.95)),
+    "latentdec128k": dict(op="latent", k=2048,
+                          gen=lambda seed=0: make_latent(32, 2, 131072, seed=seed, k_dtype=FP8_E4M3,
+                                                         decode=True)),
 }
