@@ -108,15 +108,21 @@ def copy_probe(nbytes):
 # workloads: algorithmic work of the dominant kernel
 
 def dense_flops(prob):
-    return 2.0 * prob.H * prob.D * prob.pairs()
+    """Score-contraction flops: 2 H Dk per visible pair, Dk the key row width (= D, or the latent
+    width for absorbed queries)."""
+    return 2.0 * prob.H * prob.k.shape[2] * prob.pairs()
 
 
 def decode_bytes(prob):
+    """Bytes the decode scan must read: every visible key row (+ its fp32 scale for FP8), the
+    queries it scores with (the absorbed ones for a latent cache) and the head weights."""
     import numpy as np
     kl = prob.k_len.astype(np.int64)
-    kb = prob.D * (1 if prob.k_dtype == 2 else (2 if prob.k_dtype == 1 else 4))
+    Dk = prob.k.shape[2]
+    kb = Dk * (1 if prob.k_dtype == 2 else (2 if prob.k_dtype == 1 else 4))
     per_tok = kb + (4 if prob.k_dtype == 2 else 0)
-    return float((kl * per_tok).sum() + prob.q.nbytes + prob.w.nbytes)
+    qbytes = prob.q.nbytes * Dk // prob.D
+    return float((kl * per_tok).sum() + qbytes + prob.w.nbytes)
 
 
 def group_refine_pairs(prob, G, C):
@@ -218,9 +224,9 @@ def cpu_oracle_baseline(name, spec, prob, budget_s=12.0):
                        if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    inp = oracle.Inputs(prob)
-    B, T = prob.B, prob.T
     op = spec["op"]
+    inp = oracle.Inputs(prob) if op != "latent" else None    # latent rows convert per sequence
+    B, T = prob.B, prob.T
     done_pairs = 0
     rows = 0
     t0 = time.perf_counter()
@@ -280,6 +286,25 @@ def cpu_oracle_baseline(name, spec, prob, budget_s=12.0):
                 break
         sample = (f"{rows} query rows of {B * T} in whole groups, interleaved with stride {stride} "
                   f"(pooling each of {len(pooled)} sequences once, proxy block scan + refine)")
+    elif op == "latent":
+        # the absorbed queries of the sampled rows, then the dense oracle on them
+        stride = max(1, T // 64)
+        order = [(b, t) for b in range(B) for off in range(stride) for t in range(T - 1 - off, -1, -stride)]
+        cur_b, lat = -1, None
+        for b, t in order:
+            if b != cur_b:                     # the sequence's latent rows in float64
+                ks = None if prob.k_scale is None else prob.k_scale[b]
+                cur_b, lat = b, oracle.keys_f64(prob.k[b], prob.k_dtype, ks)
+            a = oracle.absorb_queries(prob.q[b, t], prob.q_dtype, prob.wk)
+            P = oracle.visible_len(int(prob.q_pos[b, t]), int(prob.k_len[b]))
+            sc = oracle.index_scores(oracle.bf16_bits_to_f64(a["bits"]), prob.w[b, t].astype(np.float64), lat[:P])
+            oracle.select_topk(sc, np.arange(P, dtype=np.int64), spec["k"])
+            done_pairs += P
+            rows += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = (f"{rows} query rows of {B * T} (sequence by sequence, stride {stride} from the last "
+                  "row): absorbed queries + full latent prefix each")
     elif op == "given":
         G = spec["group_size"]
         banks = W.make_banks(prob, G, spec["n_cand"], 0)
@@ -356,9 +381,13 @@ class Run:
         self.op = op = spec["op"]
         self.out_idx = torch.empty((B, T, k), dtype=torch.int32, device="cuda:0")
         self.out_sc = torch.empty((B, T, k), dtype=torch.float32, device="cuda:0")
-        p = idx.make_problem(t["q"], t["k"], t["w"], t["q_pos"], t["k_len"], t["k_scale"], t["q_scale"])
+        self.q_lat = None
+        if op == "latent":
+            self.q_lat = torch.empty((B, T, prob.H, prob.k.shape[2]), dtype=torch.bfloat16, device="cuda:0")
+        p = idx.make_problem(t["q"] if self.q_lat is None else self.q_lat, t["k"], t["w"], t["q_pos"],
+                             t["k_len"], t["k_scale"], t["q_scale"])
         self.banks_np = None
-        if op == "dense":
+        if op in ("dense", "latent"):
             need = idx.workspace_bytes(idx.OP_SCORE_TOPK, p, k)
         elif op == "group":
             need = idx.workspace_bytes(idx.OP_GROUP, p, k, spec["group_size"], spec["n_cand"])
@@ -388,6 +417,9 @@ class Run:
         if op == "dense":
             idx.score_topk(t["q"], t["k"], t["w"], t["q_pos"], topk=k, k_scale=t["k_scale"],
                            q_scale=t["q_scale"], **kw)
+        elif op == "latent":
+            idx.absorb_queries(t["q"], t["wk"], out=self.q_lat)
+            idx.score_topk(self.q_lat, t["k"], t["w"], t["q_pos"], topk=k, k_scale=t["k_scale"], **kw)
         elif op == "group":
             idx.group_proxy_refine(t["q"], t["k"], t["w"], t["q_pos"], topk=k,
                                    group_size=spec["group_size"], n_cand=spec["n_cand"],
@@ -434,7 +466,7 @@ class Run:
         self.steps = steps
         self.kernels = {n: idx.timer_read(n)
                         for n in ("score", "topk", "sort", "proxy", "pool", "block_refine", "reuse",
-                                  "decode_scan", "decode_select")}
+                                  "decode_scan", "decode_select", "absorb")}
         idx.timer_enable(False)
         log(f"[bench] {self.name}: {self.ms_step:.4f} ms/step; per-kernel ms/step: " + ", ".join(
             f"{n} {ms / steps:.3f} ({c // max(1, steps)} launches)"
@@ -471,9 +503,12 @@ class Run:
                "N": prob.N, "k": self.k, "q_dtype": W.DTYPE_NAMES[prob.q_dtype],
                "k_dtype": W.DTYPE_NAMES[prob.k_dtype], "seed": self.seed,
                "pairs_per_step": prob.pairs()}
-        if op == "dense" and self.kernels["decode_scan"][1] == 0:
+        if op == "latent":
+            cfg.update(latent_width=prob.k.shape[2],
+                       absorb_ms_per_step=self.kernels["absorb"][0] / self.steps)
+        if op in ("dense", "latent") and self.kernels["decode_scan"][1] == 0:
             roof = self._mfma("score_kernel", dense_flops(prob))
-        elif op == "dense":
+        elif op in ("dense", "latent"):
             # decode shape: the streaming scan is the dominant kernel, bound by the key-cache read
             ms, n = self.kernels["decode_scan"]
             byts = decode_bytes(prob)
@@ -570,7 +605,7 @@ class Run:
         out = {"ms_per_step": self.ms_step, "value": prob.pairs() / (self.ms_step * 1e-3),
                "unit": "pairs/s", "topk_rows_per_s": prob.B * prob.T / (self.ms_step * 1e-3),
                "config": cfg, "roofline": roof, "wall_s_timed": self.wall}
-        if self.op != "dense":
+        if self.op not in ("dense", "latent"):
             log(f"[bench] {self.name}: recall vs the dense indexer")
             out["recall_vs_dense"] = self.recall_vs_dense()
         out["cpu_baseline"] = None
@@ -581,7 +616,7 @@ class Run:
 
     def free(self):
         import torch
-        for a in ("t", "out_idx", "out_sc", "ws", "banks", "pooled"):
+        for a in ("t", "out_idx", "out_sc", "ws", "banks", "pooled", "q_lat"):
             if hasattr(self, a):
                 delattr(self, a)
         torch.cuda.empty_cache()

@@ -165,6 +165,21 @@ int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
  * IDX_ERR_ALIGN (k or pooled not 16-byte aligned). */
 int idx_block_pool(const idx_problem* p, int32_t block_size, void* pooled, void* stream);
 
+/* Absorbed queries for a layer that scores a shared latent cache ("LatentIndex: Cross-Layer
+ * Sharing with Layer-Specific Selection for Sparse Attention", abstract: a layer group shares one
+ * latent cache, and each layer scores it by absorbing its key decoder into its queries instead of
+ * rebuilding its own keys). With the layer's key k[s] = latent[s] . wk (decoder wk [Dc, D]),
+ * q . k[s] = (wk q) . latent[s], so
+ *   q_lat[r, h, j] = bf16 nearest-even of sum_d q[r, h, d] * wk[j, d]   (fp32 accumulation)
+ * for rows r < rows (B * T), heads h < H, j < Dc. q: bf16 [rows, H, D]; wk: bf16 [Dc, D];
+ * q_lat: bf16 [rows, H, Dc], caller-owned device memory. The absorbed queries then go to any
+ * entry point of this library as its queries, with the latent cache [B, N, Dc] (bf16, fp32 or FP8
+ * with per-token scales) as its keys and D = Dc. Errors: IDX_ERR_INVALID_ARG (null pointer,
+ * rows or H < 1), IDX_ERR_UNSUPPORTED (D or Dc not 32, 64 or 128), IDX_ERR_ALIGN (a pointer not
+ * 16-byte aligned). */
+int idx_absorb_queries(const void* q, int32_t rows, int32_t H, int32_t D, const void* wk, int32_t Dc,
+                       void* q_lat, void* stream);
+
 /* idx_block_coarse_refine with the caller's pooled keys (as idx_block_pool writes them) in place
  * of pooling inside the call; `pooled` is required and 16-byte aligned. Same results. */
 int idx_block_coarse_refine_pooled(const idx_problem* p, int32_t k, int32_t block_size,

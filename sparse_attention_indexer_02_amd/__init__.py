@@ -29,7 +29,7 @@ import torch
 
 __all__ = ["F32", "BF16", "FP8_E4M3", "IdxError", "lib", "score_topk", "score_topk_noalloc",
            "group_proxy_refine",
-           "block_coarse_refine", "refine_given", "group_proxy_reuse", "group_block_refine", "block_pool",
+           "block_coarse_refine", "refine_given", "group_proxy_reuse", "group_block_refine", "block_pool", "absorb_queries",
            "workspace_bytes", "timer_enable", "timer_read", "EXPORTS"]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
@@ -38,7 +38,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidx.so")
 EXPORTS = ["idx_score_topk", "idx_score_topk_noalloc", "idx_group_proxy_refine", "idx_block_coarse_refine",
            "idx_refine_given", "idx_group_proxy_reuse", "idx_group_block_refine",
            "idx_group_block_workspace_bytes", "idx_workspace_bytes", "idx_strerror", "idx_timer_enable",
-           "idx_timer_read", "idx_block_pool", "idx_block_coarse_refine_pooled", "idx_group_block_refine_pooled"]
+           "idx_timer_read", "idx_block_pool", "idx_block_coarse_refine_pooled", "idx_group_block_refine_pooled",
+           "idx_absorb_queries"]
 
 
 class IdxError(RuntimeError):
@@ -74,6 +75,7 @@ def lib() -> ctypes.CDLL:
         L.idx_group_proxy_reuse.argtypes = [P, i32, i32, vp, vp, vp, sz, vp]
         L.idx_group_block_refine.argtypes = [P, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.idx_block_pool.argtypes = [P, i32, vp, vp]
+        L.idx_absorb_queries.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp]
         L.idx_block_coarse_refine_pooled.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.idx_group_block_refine_pooled.argtypes = [P, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.idx_group_block_workspace_bytes.argtypes = [P, i32, i32, i32, i32]
@@ -88,7 +90,8 @@ def lib() -> ctypes.CDLL:
         for f in ("idx_score_topk", "idx_score_topk_noalloc", "idx_group_proxy_refine", "idx_block_coarse_refine",
                   "idx_refine_given", "idx_group_proxy_reuse", "idx_group_block_refine",
                   "idx_timer_enable", "idx_timer_read", "idx_block_pool",
-                  "idx_block_coarse_refine_pooled", "idx_group_block_refine_pooled"):
+                  "idx_block_coarse_refine_pooled", "idx_group_block_refine_pooled",
+                  "idx_absorb_queries"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -262,6 +265,22 @@ def block_pool(k, block_size: int = 128, k_len=None, k_scale=None, out=None, str
     p = Problem(B, 1, 1, D, N, BF16, kc, None, _ptr(k), _ptr(k_scale) if kc == FP8_E4M3 else None, None,
                 None, _ptr(k_len), None)
     _check(lib().idx_block_pool(ctypes.byref(p), block_size, _ptr(out), _stream(k, stream)), "idx_block_pool")
+    return out
+
+
+def absorb_queries(q, wk, out=None, stream=None):
+    """Absorbed queries of a layer scoring a shared latent cache (idx_absorb_queries): bf16
+    q [B,T,H,D] and key decoder wk [Dc,D] -> bf16 [B,T,H,Dc]."""
+    if q.dim() != 4 or wk.dim() != 2 or wk.shape[1] != q.shape[3]:
+        raise IdxError("expected q [B,T,H,D] and wk [Dc,D]")
+    if q.dtype != torch.bfloat16 or wk.dtype != torch.bfloat16:
+        raise IdxError("absorb_queries takes bf16 queries and decoder")
+    B, T, H, D = q.shape
+    Dc = wk.shape[0]
+    if out is None:
+        out = torch.empty((B, T, H, Dc), dtype=torch.bfloat16, device=q.device)
+    _check(lib().idx_absorb_queries(_ptr(q), B * T, H, D, _ptr(wk), Dc, _ptr(out), _stream(q, stream)),
+           "idx_absorb_queries")
     return out
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libidx.so")
 SOURCES = ["abi.hip", "score.hip", "score_f8f8.hip", "score_bb128.hip", "score_bb64.hip", "score_bb32_b8.hip",
            "score_f32_f32_d128.hip", "score_f32_bf16_d128.hip", "score_f32_fp8_d128.hip",
            "score_f32_f32_d32_64.hip", "score_f32_bf16_d32_64.hip", "score_f32_fp8_d32_64.hip",
-           "block_refine.hip", "decode.hip", "topk.hip", "prep.hip"]
+           "block_refine.hip", "decode.hip", "topk.hip", "prep.hip", "latent.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

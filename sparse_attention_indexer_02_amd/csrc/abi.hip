@@ -955,6 +955,21 @@ int idx_block_coarse_refine(const idx_problem* p, int32_t k, int32_t block_size,
   }
 }
 
+int idx_absorb_queries(const void* q, int32_t rows, int32_t H, int32_t D, const void* wk, int32_t Dc,
+                       void* q_lat, void* stream) {
+  try {
+    if (!q || !wk || !q_lat || rows < 1 || H < 1) return IDX_ERR_INVALID_ARG;
+    if ((D != 32 && D != 64 && D != 128) || (Dc != 32 && Dc != 64 && Dc != 128)) return IDX_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(wk, 16) || !aligned(q_lat, 16)) return IDX_ERR_ALIGN;
+    const int64_t M = (int64_t)rows * H;
+    if ((M + 1023) / 1024 > 0x7FFFFFFF) return IDX_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return from_hip(timed("absorb", s, [&] { return launch_absorb(q, wk, q_lat, M, D, Dc, s); }));
+  } catch (...) {
+    return IDX_ERR_INTERNAL;
+  }
+}
+
 int idx_block_pool(const idx_problem* p, int32_t block_size, void* pooled, void* stream) {
   try {
     return pool_impl(p, block_size, pooled, static_cast<hipStream_t>(stream));

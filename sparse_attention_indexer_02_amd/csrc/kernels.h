@@ -150,6 +150,8 @@ bool decode_supported(int q_dtype, int k_dtype, int H, int D, int T, int N);
 bool decode_blocks_supported(int q_dtype, int k_dtype, int H, int D, int T, int N, int block_size, int keep);
 hipError_t launch_decode_scan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_select(const DecodeArgs& a, hipStream_t s);
+// absorbed queries: out[m, j] = bf16(sum_d q[m, d] * wk[j, d]) for m < M (bf16 [M, D], [Dc, D], [M, Dc])
+hipError_t launch_absorb(const void* q, const void* wk, void* out, int64_t M, int D, int Dc, hipStream_t s);
 
 constexpr int KEY_TILE = 64;       // keys per LDS tile of the score kernels
 constexpr int Q_TILE = 8;          // queries per work-group tile (one per wave)

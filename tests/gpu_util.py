@@ -10,8 +10,8 @@ import workloads as W
 
 
 def dev(prob: W.Problem, device="cuda"):
-    """Returns dict(q, k, w, q_pos, k_len, k_scale, q_scale) of device tensors holding the same
-    bytes."""
+    """Returns dict(q, k, w, q_pos, k_len, k_scale, q_scale, wk) of device tensors holding the
+    same bytes."""
     if prob.q_dtype == W.BF16:
         q = torch.from_numpy(prob.q.view(np.int16)).view(torch.bfloat16)
     elif prob.q_dtype == W.FP8_E4M3:
@@ -32,6 +32,9 @@ def dev(prob: W.Problem, device="cuda"):
     out["q_scale"] = None
     if getattr(prob, "q_scale", None) is not None:
         out["q_scale"] = torch.from_numpy(prob.q_scale).to(device)
+    out["wk"] = None
+    if getattr(prob, "wk", None) is not None:
+        out["wk"] = torch.from_numpy(prob.wk.view(np.int16)).view(torch.bfloat16).to(device)
     return out
 
 

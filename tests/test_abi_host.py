@@ -187,3 +187,12 @@ def test_binding_rejects_host_tensors():
         idx.make_problem(q, k, w, pos)
     with pytest.raises(idx.IdxError):
         idx.make_problem(q, k[:, :, :16], w, pos)
+
+
+def test_absorb_arguments(L):
+    a = lambda q=0x10000, rows=4, H=2, D=128, wk=0x20000, Dc=64, out=0x30000: L.idx_absorb_queries(
+        q, rows, H, D, wk, Dc, out, None)
+    assert a(q=None) == -1 and a(wk=None) == -1 and a(out=None) == -1
+    assert a(rows=0) == -1 and a(H=0) == -1
+    assert a(D=96) == -2 and a(Dc=16) == -2
+    assert a(q=0x10008) == -3 and a(wk=0x20002) == -3 and a(out=0x30004) == -3
