@@ -18,6 +18,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kScoreBudget = size_t(1) << 30;     // score rows held per chunk (bytes)
+constexpr size_t kDenseBudget = size_t(13) << 27;    // dense rows (1.625 GiB: candidate lists)
 constexpr int kTargetGroups = 1024;                  // work-groups wanted per score launch
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -124,19 +125,35 @@ int key_split(int n_groups, int n_keys, int* split_keys, int target = kTargetGro
 
 struct DensePlan {
   int chunkT;
+  int64_t stride;      // floats per score row
+  bool self_select;
   float* scores;
   int32_t* row_len;
   int32_t* meta;
   size_t bytes;
 };
 
+// bf16 x bf16 and FP8 x FP8 rows of up to 65536 slots: each score-kernel wave selects its own
+// row, from a candidate list of scores and 16-bit slots (rows 1.5x the slot count, plus room for
+// one more store of 64 entries)
+bool dense_self_select(const idx_problem* p) {
+  return ((p->q_dtype == IDX_BF16 && p->k_dtype == IDX_BF16) ||
+          (p->q_dtype == IDX_FP8_E4M3 && p->k_dtype == IDX_FP8_E4M3)) &&
+         p->N <= 65536;
+}
+
 // score rows are held in chunks of at most `row_budget` bytes
-DensePlan plan_dense(const idx_problem* p, void* ws, size_t row_budget = kScoreBudget) {
+DensePlan plan_dense(const idx_problem* p, void* ws, size_t row_budget = kDenseBudget) {
   DensePlan d;
   Carver c(ws);
-  d.chunkT = (int)std::max<int64_t>(
-      1, std::min<int64_t>(p->T, (int64_t)row_budget / std::max<int64_t>(1, (int64_t)p->B * rstride(p->N) * 4)));
-  d.scores = c.take<float>((size_t)p->B * d.chunkT * rstride(p->N));
+  d.self_select = dense_self_select(p);
+  d.stride = d.self_select ? rstride(p->N + 64) + rstride(p->N + 64) / 2 : rstride(p->N);
+  int64_t rows = std::max<int64_t>(1, (int64_t)row_budget / std::max<int64_t>(1, (int64_t)p->B * d.stride * 4));
+  // whole multiples of 2048 queries (256 work-groups of 8) when that many fit, so that each
+  // launch fills the compute units evenly
+  if (rows >= 2048 && rows < p->T) rows = rows / 2048 * 2048;
+  d.chunkT = (int)std::min<int64_t>(p->T, rows);
+  d.scores = c.take<float>((size_t)p->B * d.chunkT * d.stride);
   d.row_len = c.take<int32_t>((size_t)p->B * d.chunkT);
   d.meta = c.take<int32_t>((size_t)p->B * d.chunkT * 4);
   d.bytes = c.off + kAlign;
@@ -462,7 +479,7 @@ int decode_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_sc
 }
 
 int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* out_score,
-                    void* ws, size_t ws_bytes, hipStream_t s, size_t row_budget = kScoreBudget) {
+                    void* ws, size_t ws_bytes, hipStream_t s, size_t row_budget = kDenseBudget) {
   int st = validate(p, k, out_idx, out_score);
   if (st) return st;
   if (use_decode(p)) return decode_impl(p, k, out_idx, out_score, ws, ws_bytes, s);
@@ -473,20 +490,18 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
     const int c1 = std::min(p->T, c0 + pl.chunkT);
     ScoreArgs a = base_score_args(p);
     a.c0 = c0; a.c1 = c1;
-    a.scores = pl.scores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
+    a.scores = pl.scores; a.score_stride = pl.stride; a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
-    // bf16 rows of up to 65536 slots: each score-kernel wave selects its own row
-    const bool self_select = ((p->q_dtype == IDX_BF16 && p->k_dtype == IDX_BF16) ||
-                              (p->q_dtype == IDX_FP8_E4M3 && p->k_dtype == IDX_FP8_E4M3)) &&
-                             p->N <= 65536;
+    const bool self_select = pl.self_select;
     if (self_select) {
       a.sel_idx = out_idx; a.sel_score = out_score; a.sel_T = p->T;
+      a.slot_off = (int)rstride(p->N + 64);
     }
     bool fused;
     if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s, self_select ? cu_count() : kTargetGroups))))
       return st;
     if (fused && self_select) continue;
-    TopkArgs t = topk_args(pl.scores, rstride(p->N), pl.row_len, p->B * (c1 - c0), k, c1 - c0, p->T, c0,
+    TopkArgs t = topk_args(pl.scores, pl.stride, pl.row_len, p->B * (c1 - c0), k, c1 - c0, p->T, c0,
                            out_idx, out_score, k);
     t.row_meta = fused ? pl.meta : nullptr;
     t.digit_bits = a.digit_bits;

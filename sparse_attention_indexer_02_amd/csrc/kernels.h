@@ -38,8 +38,12 @@ struct ScoreArgs {
   int tiles_per_seq;
   int split_keys;                  // keys per grid.y split (multiple of the key tile)
   // optional selection by the score kernel itself (key range, bf16, one key split, 12-bit
-  // summary): the top topk_k slots of row (b, t) go to sel_idx/sel_score [B, sel_T, topk_k]
+  // summary): the top topk_k slots of row (b, t) go to sel_idx/sel_score [B, sel_T, topk_k].
+  // The row then holds a candidate list: scores from the row start, 16-bit slots from float
+  // offset slot_off (score_stride >= slot_off * 3 / 2, slot_off >= rows' slots + 64, a multiple
+  // of 64)
   int32_t* sel_idx; float* sel_score; int sel_T;
+  int slot_off;
 };
 
 // Pick rows from per-row score arrays: the top-k slots of each row (a set; with a row summary

@@ -29,25 +29,27 @@ template <class Mma, int KST> struct TileKeys {
   static constexpr int value = Direct<Mma, KST>::value ? 128 : 64;
 };
 
-// One wave selects the top k slots of its own score row (n <= 65536 slots) from the row's 12-bit
-// first-digit summary: tot finite slots, bin b1 of the k-th largest key, `above` slots in higher
-// bins and `inbin` slots in bin b1. One pass over the row writes the slots above bin b1 to the
-// output and keeps the slots of bin b1:
+// One wave selects the top k slots of its own score row from the row's candidate list: n
+// entries, entry i holding a score (srow[i]) and its 16-bit slot (sslot[i]); the list holds every
+// finite slot at or above a bound no higher than the final first-digit bin b1 (the score kernel
+// writes it while it scores the row), and the row's 12-bit first-digit summary counts every finite
+// slot: tot finite slots, bin b1 of the k-th largest key, `above` slots in higher bins and `inbin`
+// slots in bin b1. One pass over the list writes the entries above bin b1 to the output and keeps
+// the entries of bin b1:
 //   - when they fit (inbin <= CAP) as (key, slot) pairs in LDS (keys in `ck`, 16-bit slots in the
 //     upper half of `h`);
-//   - otherwise compacted into the row itself: entry p (written over slot p, which this wave has
-//     already read, since p counts a subset of the slots read so far) holds the key's low 20 bits
-//     and the slot's low 12 bits; the slot's upper bits come from a table of the entry count
-//     before each 4096-slot block (h[1024..1041)), and the key's upper 12 bits are b1. The 10-bit
-//     histogram of the next digit is built during the pass.
-// The k-th key is then resolved on the kept slots digit by digit: 10 more bits give its 22-bit
-// prefix; slots above the prefix are written, and the slots sharing it (at most 256) are ranked
-// exactly, higher key first, then lower slot (ties keep the lowest slots); a prefix shared by more
-// slots takes a last 10-bit digit and keeps the lowest slots equal to the k-th key. Histograms use
-// 1024 words of `h`. Row reads are eight 16-byte loads per lane at a time. Output order: pass
-// order, slot order within a pass.
+//   - otherwise compacted into the list itself: entry p (key over srow[p], slot over sslot[p],
+//     which this wave has already read, since p counts a subset of the entries read so far). The
+//     10-bit histogram of the next digit is built during the pass.
+// The k-th key is then resolved on the kept entries digit by digit: 10 more bits give its 22-bit
+// prefix; entries above the prefix are written, and the entries sharing it (at most 256) are
+// ranked exactly, higher key first, then lower slot (ties keep the lowest slots); a prefix shared
+// by more entries takes a last 10-bit digit and keeps the lowest slots equal to the k-th key (the
+// list is in ascending slot order). Histograms use 1024 words of `h`. List reads are eight
+// 16-byte score loads and eight 8-byte slot loads per lane at a time; `last` is the highest
+// index a 4-entry load may start at. Output order: pass order, list order within a pass.
 template <int CAP>
-__device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stride, int k,
+__device__ __forceinline__ void wave_select_row(float* srow, uint16_t* sslot, int n, int last, int k,
                                                 uint32_t tot, int b1, uint32_t above, uint32_t inbin,
                                                 uint32_t* h, uint32_t* ck, int32_t* oidx, float* osc) {
   static_assert(CAP <= 2048, "16-bit slots in 1024 words");
@@ -56,61 +58,65 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
   const uint32_t kk = min((uint32_t)k, tot);
   const bool all = kk == tot;
   const bool lds = !all && inbin <= (uint32_t)CAP;   // bin b1 kept as LDS pairs
-  const bool glob = !all && !lds;                     // bin b1 compacted into the row
+  const bool glob = !all && !lds;                     // bin b1 compacted into the list
   uint16_t* cs = reinterpret_cast<uint16_t*>(h + 1024);
-  uint32_t* blk = h + 1024;                           // glob: entries before each 4096-slot block
   uint32_t* crow = reinterpret_cast<uint32_t*>(srow);
-  const int nblk = (n + 4095) >> 12;
-  const int last = (int)stride - 4;
-  // visits the row 256 slots at a time: f(i0, key[4], v) with key 0 past the row. The loads of
-  // the next 256 U slots are in flight while the current ones are processed (two register
-  // buffers); addresses are clamped into the row's allocation. f may overwrite slots below the
-  // end of the block it processes: the loads in flight are all at or above it.
+  // visits the list 256 entries at a time: f(i0, key[4], v, slot[4]) with key 0 past the list.
+  // The loads of the next 256 U entries are in flight while the current ones are processed (two
+  // register buffers); indexes are clamped into the row's allocation. f may overwrite entries
+  // below the end of the block it processes: the loads in flight are all at or above it.
   auto stream = [&](auto f) {
     f32x4_t va[U], vb[U];
-    auto load = [&](int i0, f32x4_t (&v)[U]) {
+    u32x2_t sa[U], sb[U];
+    auto load = [&](int i0, f32x4_t (&v)[U], u32x2_t (&sv)[U]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        v[u] = *reinterpret_cast<const f32x4_t*>(srow + min(i0 + 256 * u + 4 * lane, last));
+      for (int u = 0; u < U; ++u) {
+        const int j = min(i0 + 256 * u + 4 * lane, last);
+        v[u] = *reinterpret_cast<const f32x4_t*>(srow + j);
+        sv[u] = *reinterpret_cast<const u32x2_t*>(sslot + j);
+      }
     };
-    auto run = [&](int i0, const f32x4_t (&v)[U]) {
+    auto run = [&](int i0, const f32x4_t (&v)[U], const u32x2_t (&sv)[U]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j0 = i0 + 256 * u;
         if (j0 >= n) break;
-        uint32_t key[4];
+        uint32_t key[4], sl[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[e] = j0 + 4 * lane + e < n ? f2key(v[u][e]) : 0u;
-        f(j0, key, v[u]);
+        for (int e = 0; e < 4; ++e) {
+          key[e] = j0 + 4 * lane + e < n ? f2key(v[u][e]) : 0u;
+          sl[e] = (sv[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        }
+        f(j0, key, v[u], sl);
       }
     };
-    load(0, va);
+    load(0, va, sa);
     for (int i0 = 0; i0 < n; i0 += 512 * U) {
-      load(i0 + 256 * U, vb);
-      run(i0, va);
+      load(i0 + 256 * U, vb, sb);
+      run(i0, va, sa);
       if (i0 + 256 * U >= n) break;
-      load(i0 + 512 * U, va);
-      run(i0 + 256 * U, vb);
+      load(i0 + 512 * U, va, sa);
+      run(i0 + 256 * U, vb, sb);
     }
   };
   uint32_t pos = 0;
-  // writes the slots flagged in sel[4] at pos, in slot order (never past the k outputs, whatever
-  // the summary says)
-  auto emit = [&](int i0, const bool (&sel)[4], const f32x4_t& v) {
+  // writes the entries flagged in sel[4] at pos, in list order (never past the k outputs,
+  // whatever the summary says)
+  auto emit = [&](const bool (&sel)[4], const f32x4_t& v, const uint32_t (&sl)[4]) {
     const uint32_t c = (sel[0] ? 1u : 0u) + (sel[1] ? 1u : 0u) + (sel[2] ? 1u : 0u) + (sel[3] ? 1u : 0u);
     const uint32_t inc = wave_scan_dpp(c);
     uint32_t p = pos + inc - c;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (sel[e] && p < (uint32_t)k) {
-        oidx[p] = i0 + 4 * lane + e;
+        oidx[p] = (int32_t)sl[e];
         if (osc) osc[p] = v[e];
       }
       p += sel[e] ? 1u : 0u;
     }
     pos += wave_bcast(inc, 63);
   };
-  // writes one flagged slot per lane at pos, in lane order
+  // writes one flagged entry per lane at pos, in lane order
   auto emit1 = [&](bool sel, uint32_t slot, uint32_t key) {
     const uint32_t inc = wave_scan_dpp(sel ? 1u : 0u);
     if (sel && pos + inc - 1 < (uint32_t)k) {
@@ -140,8 +146,8 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
   };
   const uint32_t ub1 = (uint32_t)b1;
   if (glob) zero_hist();
-  uint32_t cb = 0;                                       // kept slots of bin b1
-  stream([&](int i0, const uint32_t (&key)[4], const f32x4_t& v) {
+  uint32_t cb = 0;                                       // kept entries of bin b1
+  stream([&](int i0, const uint32_t (&key)[4], const f32x4_t& v, const uint32_t (&sl)[4]) {
     bool sel[4];
     uint32_t ce = 0;
 #pragma unroll
@@ -156,48 +162,42 @@ __device__ __forceinline__ void wave_select_row(float* srow, int n, int64_t stri
       for (int e = 0; e < 4; ++e) {
         if ((key[e] >> 20) == ub1 && p < (uint32_t)CAP) {   // p < inbin for finite keys
           ck[p] = key[e];
-          cs[p] = (uint16_t)(i0 + 4 * lane + e);
+          cs[p] = (uint16_t)sl[e];
         }
         p += (key[e] >> 20) == ub1 ? 1u : 0u;
       }
       cb += wave_bcast(einc, 63);
     } else if (glob) {
-      if ((i0 & 4095) == 0 && lane == 0) blk[i0 >> 12] = cb;
       const uint32_t einc = wave_scan_dpp(ce);
-      uint32_t p = cb + einc - ce;                       // p < i0 + 256: slots already read
+      uint32_t p = cb + einc - ce;                       // p < i0 + 256: entries already read
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if ((key[e] >> 20) == ub1 && p < (uint32_t)n) {
-          crow[p] = ((key[e] & 0xFFFFFu) << 12) | ((uint32_t)(i0 + 4 * lane + e) & 0xFFFu);
+          crow[p] = key[e];
+          sslot[p] = (uint16_t)sl[e];
           atomicAdd(&h[(key[e] >> 10) & 0x3FFu], 1u);
         }
         p += (key[e] >> 20) == ub1 ? 1u : 0u;
       }
       cb += wave_bcast(einc, 63);
     }
-    emit(i0, sel, v);
+    emit(sel, v, sl);
   });
   if (!all) {
     if (glob) {
-      if (lane == 0) blk[nblk] = cb;
       // the compacted entries are read back: wait for the stores, and drop any stale copy of
-      // the row the vector L1 cache still holds
+      // the list the vector L1 cache still holds
       wait_vmem();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    // kept slot i of bin b1: its key and slot
+    // kept entry i of bin b1: its key and slot
     auto get = [&](int i, uint32_t& key, uint32_t& slot) {
       if (lds) {
         key = ck[i];
         slot = cs[i];
       } else {
-        const uint32_t e = crow[i];
-        int j = 0;                                       // block j: blk[j] <= i < blk[j + 1]
-#pragma unroll
-        for (int st = 8; st > 0; st >>= 1)
-          if (j + st < nblk && blk[j + st] <= (uint32_t)i) j += st;
-        key = (ub1 << 20) | (e >> 12);
-        slot = ((uint32_t)j << 12) | (e & 0xFFFu);
+        key = crow[i];
+        slot = sslot[i];
       }
     };
     inbin = min(inbin, min(cb, lds ? (uint32_t)CAP : (uint32_t)n));   // slots actually kept
@@ -471,6 +471,58 @@ score_kernel(ScoreArgs a) {
   // 12-bit digits count in 16-bit halves: slot 65535 (only rows of 65536 slots have it) is kept
   // out of the histogram so that no count reaches 65536; the summary adds it back
   const int xslot = a.digit_bits == 12 ? 65535 : -1;
+  // A wave that selects its own row keeps a candidate list instead of the row: every finite
+  // score at or above a running bound cbin (the first-digit bin of the k-th largest score counted
+  // so far, which never exceeds the row's final bin b1: the k-th largest of a subset is at most
+  // that of the whole), in slot order, with the 16-bit slots after the scores (sslot). The
+  // selection then reads the list instead of the whole row.
+  const bool cmp = !LISTM && fuse && a.sel_idx != nullptr && a.digit_bits == 12;   // uniform
+  uint16_t* sslot = reinterpret_cast<uint16_t*>(srow + a.slot_off);
+  uint32_t ccnt = 0, cbin = 0;                        // list entries; bound (12-bit bin)
+  // one score per lane at `slot` (inside the prefix when ok), by every lane of the wave. Without
+  // a branch: the listed scores go to the list's end, the others right after them, where the
+  // next listed scores overwrite them (the row has 64 entries of room past its slot count), so
+  // that every lane stores and the 64 stores are contiguous
+  auto put = [&](float v, int slot, bool ok) {
+    if (cmp) {
+      const uint32_t key = f2key(v);
+      const bool f = ok && key > KEY_NEG_INF && (key >> 20) >= cbin;
+      const uint64_t m = __ballot(f);
+      const uint32_t nf = (uint32_t)__popcll(m);
+      const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t at = f ? ccnt + r : ccnt + nf + ((uint32_t)lane - r);
+      srow[at] = v;
+      sslot[at] = (uint16_t)slot;
+      ccnt += nf;
+    } else if (ok) {
+      srow[slot] = v;
+    }
+  };
+  // raises the bound every 32 stored tiles: a scan of the histogram from the highest bin down,
+  // 64 bins per step, to the bin holding the k-th largest counted score (a short loop with one
+  // LDS read per lane, so that it costs the tile loop no registers). The histogram counts the
+  // listed scores only (every finite score while fewer than k are counted, then those at or
+  // above the bound): it holds every score at or above the current bound, so the k-th largest it
+  // counts is the k-th largest seen so far; and its total reaches k exactly only if those k are
+  // the row's top k, since every later score is below the bound.
+  int nflush = 0;
+  auto raise_bound = [&]() {
+    ++nflush;
+    if (cmp && (nflush & 31) == 0) {
+      uint32_t run = 0;
+      for (int top = 4095; top >= (int)cbin; top -= 64) {
+        const int q = top - lane;                        // lane 0: the highest bin of the step
+        const uint32_t c = q >= (int)cbin ? (whist[q & 2047] >> ((q >> 11) << 4)) & 0xFFFFu : 0u;
+        const uint32_t inc = wave_scan_dpp(c);
+        const uint64_t hit = __ballot(run + inc >= (uint32_t)a.topk_k);
+        if (hit) {
+          cbin = (uint32_t)(top - (int)__builtin_ctzll(hit));
+          break;
+        }
+        run += wave_bcast(inc, 63);
+      }
+    }
+  };
   float pv[NSUB / 2];
   int pbase = -1;                                     // first slot of the pending scores, or -1
 #pragma unroll
@@ -480,14 +532,16 @@ score_kernel(ScoreArgs a) {
   auto flush = [&]() {
     if (DEFER && pbase >= 0) {
       if (fuse) {
+        raise_bound();
 #pragma unroll
         for (int p = 0; p < NSUB / 2; ++p) {
           const uint32_t key = f2key(pv[p]);
-          hist1_add_if(whist, key, a.digit_bits, key > KEY_NEG_INF && pbase + p * 64 + lane != xslot);
+          hist1_add_if(whist, key, a.digit_bits,
+                       key > KEY_NEG_INF && pbase + p * 64 + lane != xslot && (!cmp || (key >> 20) >= cbin));
         }
       }
 #pragma unroll
-      for (int p = 0; p < NSUB / 2; ++p) srow[pbase + p * 64 + lane] = pv[p];
+      for (int p = 0; p < NSUB / 2; ++p) put(pv[p], pbase + p * 64 + lane, true);
       pbase = -1;
     }
   };
@@ -692,13 +746,13 @@ score_kernel(ScoreArgs a) {
           }
           if (fuse) {
             const uint32_t key = f2key(v[p]);
-            if (key > KEY_NEG_INF && base + n != xslot) hist1_add(whist, key, a.digit_bits);
+            if (key > KEY_NEG_INF && base + n != xslot && (!cmp || (key >> 20) >= cbin))
+              hist1_add(whist, key, a.digit_bits);
           }
         }
       }
 #pragma unroll
-      for (int p = 0; p < NSUB / 2; ++p)
-        if (base + p * 64 + lane < lim) srow[base + p * 64 + lane] = v[p];
+      for (int p = 0; p < NSUB / 2; ++p) put(v[p], base + p * 64 + lane, base + p * 64 + lane < lim);
     }
     lds_barrier();
   }
@@ -711,7 +765,14 @@ score_kernel(ScoreArgs a) {
     wait_vmem();                                         // this wave's score stores
     // the bin of slot 65535's key, which the histogram left out (-1 if none)
     int xbin = -1;
-    if (lim > xslot && xslot >= 0) {
+    if (cmp) {
+      // slot 65535 is the list's last entry when it was kept; a key below the bound is not
+      // counted, like every other one (see raise_bound)
+      if (ccnt > 0 && lim > xslot && xslot >= 0 && sslot[ccnt - 1] == (uint16_t)xslot) {
+        const uint32_t xk = f2key(srow[ccnt - 1]);
+        if (xk > KEY_NEG_INF) xbin = (int)digit1(xk, bits);
+      }
+    } else if (lim > xslot && xslot >= 0) {
       const uint32_t xk = f2key(srow[xslot]);
       if (xk > KEY_NEG_INF) xbin = (int)digit1(xk, bits);
     }
@@ -732,11 +793,11 @@ score_kernel(ScoreArgs a) {
       m[META_INBIN] = (int32_t)inbin;
     }
     if constexpr (!LISTM) {
-      if (a.sel_idx != nullptr && bits == 12) {
+      if (cmp) {
         // the wave's share of the key tiles (idle after the last tile) holds bin b1's keys
         constexpr int SLICE = 2 * G::TILE_BYTES / NW / 4;
         wave_select_row<SLICE < 2048 ? SLICE : 2048>(
-            srow, my_count, a.score_stride, a.topk_k, tot, bin, above, inbin, whist,
+            srow, sslot, (int)ccnt, a.slot_off - 4, a.topk_k, tot, bin, above, inbin, whist,
             reinterpret_cast<uint32_t*>(tiles + wave * (2 * G::TILE_BYTES / NW)),
             a.sel_idx + ((int64_t)b * a.sel_T + t) * a.topk_k,
                         a.sel_score ? a.sel_score + ((int64_t)b * a.sel_T + t) * a.topk_k : nullptr);
