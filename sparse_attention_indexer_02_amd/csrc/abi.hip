@@ -496,6 +496,10 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
     if (self_select) {
       a.sel_idx = out_idx; a.sel_score = out_score; a.sel_T = p->T;
       a.slot_off = (int)rstride(p->N + 64);
+      // candidate lists pay off on long rows (the row's read-back shrinks to the list, for some
+      // extra work per tile); a prefill chunk's queries sit at the end of the cache, so the
+      // chunk's longest row is about N - T + c1 slots
+      a.sel_list = std::min<int64_t>(p->N, (int64_t)p->N - p->T + c1) > 32768 ? 1 : 0;
     }
     bool fused;
     if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s, self_select ? cu_count() : kTargetGroups))))

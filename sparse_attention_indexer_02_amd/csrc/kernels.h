@@ -39,11 +39,11 @@ struct ScoreArgs {
   int split_keys;                  // keys per grid.y split (multiple of the key tile)
   // optional selection by the score kernel itself (key range, bf16, one key split, 12-bit
   // summary): the top topk_k slots of row (b, t) go to sel_idx/sel_score [B, sel_T, topk_k].
-  // The row then holds a candidate list: scores from the row start, 16-bit slots from float
-  // offset slot_off (score_stride >= slot_off * 3 / 2, slot_off >= rows' slots + 64, a multiple
-  // of 64)
+  // Rows then have room for 16-bit slots from float offset slot_off (score_stride >= slot_off *
+  // 3 / 2, slot_off >= rows' slots + 64, a multiple of 64); with sel_list the row holds a
+  // candidate list (scores from the row start, their slots there) instead of every slot
   int32_t* sel_idx; float* sel_score; int sel_T;
-  int slot_off;
+  int slot_off, sel_list;
 };
 
 // Pick rows from per-row score arrays: the top-k slots of each row (a set; with a row summary

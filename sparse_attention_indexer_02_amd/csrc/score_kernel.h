@@ -29,8 +29,10 @@ template <class Mma, int KST> struct TileKeys {
   static constexpr int value = Direct<Mma, KST>::value ? 128 : 64;
 };
 
-// One wave selects the top k slots of its own score row from the row's candidate list: n
-// entries, entry i holding a score (srow[i]) and its 16-bit slot (sslot[i]); the list holds every
+// One wave selects the top k slots of its own score row from the row's candidate list (LIST: n
+// entries, entry i holding a score (srow[i]) and its 16-bit slot (sslot[i])) or from the row itself
+// (!LIST: n slots, entry i is slot i; sslot is then only the room the compaction below uses). A
+// list holds every
 // finite slot at or above a bound no higher than the final first-digit bin b1 (the score kernel
 // writes it while it scores the row), and the row's 12-bit first-digit summary counts every finite
 // slot: tot finite slots, bin b1 of the k-th largest key, `above` slots in higher bins and `inbin`
@@ -48,7 +50,7 @@ template <class Mma, int KST> struct TileKeys {
 // list is in ascending slot order). Histograms use 1024 words of `h`. List reads are eight
 // 16-byte score loads and eight 8-byte slot loads per lane at a time; `last` is the highest
 // index a 4-entry load may start at. Output order: pass order, list order within a pass.
-template <int CAP>
+template <int CAP, bool LIST>
 __device__ __forceinline__ void wave_select_row(float* srow, uint16_t* sslot, int n, int last, int k,
                                                 uint32_t tot, int b1, uint32_t above, uint32_t inbin,
                                                 uint32_t* h, uint32_t* ck, int32_t* oidx, float* osc) {
@@ -73,7 +75,7 @@ __device__ __forceinline__ void wave_select_row(float* srow, uint16_t* sslot, in
       for (int u = 0; u < U; ++u) {
         const int j = min(i0 + 256 * u + 4 * lane, last);
         v[u] = *reinterpret_cast<const f32x4_t*>(srow + j);
-        sv[u] = *reinterpret_cast<const u32x2_t*>(sslot + j);
+        if constexpr (LIST) sv[u] = *reinterpret_cast<const u32x2_t*>(sslot + j);
       }
     };
     auto run = [&](int i0, const f32x4_t (&v)[U], const u32x2_t (&sv)[U]) {
@@ -85,7 +87,8 @@ __device__ __forceinline__ void wave_select_row(float* srow, uint16_t* sslot, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           key[e] = j0 + 4 * lane + e < n ? f2key(v[u][e]) : 0u;
-          sl[e] = (sv[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          if constexpr (LIST) sl[e] = (sv[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          else sl[e] = (uint32_t)(j0 + 4 * lane + e);
         }
         f(j0, key, v[u], sl);
       }
@@ -256,7 +259,7 @@ __device__ __forceinline__ void wave_select_row(float* srow, uint16_t* sslot, in
   }
 }
 
-template <class Mma, int D, int HB, int KST, bool LISTM>
+template <class Mma, int D, int HB, int KST, bool LISTM, bool CMP>
 __global__ void __launch_bounds__(WavesFor<HB>::value * 64)
 score_kernel(ScoreArgs a) {
   constexpr int NW = WavesFor<HB>::value;
@@ -476,7 +479,7 @@ score_kernel(ScoreArgs a) {
   // so far, which never exceeds the row's final bin b1: the k-th largest of a subset is at most
   // that of the whole), in slot order, with the 16-bit slots after the scores (sslot). The
   // selection then reads the list instead of the whole row.
-  const bool cmp = !LISTM && fuse && a.sel_idx != nullptr && a.digit_bits == 12;   // uniform
+  const bool cmp = CMP && !LISTM && fuse && a.sel_idx != nullptr && a.digit_bits == 12;   // uniform
   uint16_t* sslot = reinterpret_cast<uint16_t*>(srow + a.slot_off);
   uint32_t ccnt = 0, cbin = 0;                        // list entries; bound (12-bit bin)
   // one score per lane at `slot` (inside the prefix when ok), by every lane of the wave. Without
@@ -793,11 +796,11 @@ score_kernel(ScoreArgs a) {
       m[META_INBIN] = (int32_t)inbin;
     }
     if constexpr (!LISTM) {
-      if (cmp) {
+      if (a.sel_idx != nullptr && bits == 12) {
         // the wave's share of the key tiles (idle after the last tile) holds bin b1's keys
         constexpr int SLICE = 2 * G::TILE_BYTES / NW / 4;
-        wave_select_row<SLICE < 2048 ? SLICE : 2048>(
-            srow, sslot, (int)ccnt, a.slot_off - 4, a.topk_k, tot, bin, above, inbin, whist,
+        wave_select_row<SLICE < 2048 ? SLICE : 2048, CMP>(
+            srow, sslot, CMP ? (int)ccnt : my_count, a.slot_off - 4, a.topk_k, tot, bin, above, inbin, whist,
             reinterpret_cast<uint32_t*>(tiles + wave * (2 * G::TILE_BYTES / NW)),
             a.sel_idx + ((int64_t)b * a.sel_T + t) * a.topk_k,
                         a.sel_score ? a.sel_score + ((int64_t)b * a.sel_T + t) * a.topk_k : nullptr);
@@ -816,8 +819,9 @@ hipError_t launch_one(const ScoreArgs& a, int n_splits, hipStream_t s) {
   typedef Geo<Mma, D, KT> G;
   const size_t lds = 2 * G::TILE_BYTES + 4 * KT * sizeof(int32_t) +
                      (a.row_meta ? (size_t)NW * 2048 * sizeof(uint32_t) : 0);
-  auto kfn = a.mode == MODE_LIST ? score_kernel<Mma, D, HB, KST, true>
-                                 : score_kernel<Mma, D, HB, KST, false>;
+  auto kfn = a.mode == MODE_LIST ? score_kernel<Mma, D, HB, KST, true, false>
+             : a.sel_list       ? score_kernel<Mma, D, HB, KST, false, true>
+                                : score_kernel<Mma, D, HB, KST, false, false>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
