@@ -107,8 +107,8 @@ struct Carver {
   }
 };
 
-int chunk_rows(int B, int64_t row_bytes, int rows) {
-  int64_t c = (int64_t)kScoreBudget / std::max<int64_t>(1, (int64_t)B * row_bytes);
+int chunk_rows(int B, int64_t row_bytes, int rows, size_t budget = kScoreBudget) {
+  int64_t c = (int64_t)budget / std::max<int64_t>(1, (int64_t)B * row_bytes);
   c = std::max<int64_t>(1, std::min<int64_t>(c, rows));
   return (int)c;
 }
@@ -142,12 +142,36 @@ bool dense_self_select(const idx_problem* p) {
          p->N <= 65536;
 }
 
+// floats per score row of a RANGE scan whose rows may be selected by the score kernel itself
+int64_t self_select_stride(const idx_problem* p) {
+  return dense_self_select(p) ? rstride(p->N + 64) + rstride(p->N + 64) / 2 : rstride(p->N);
+}
+
+// The score kernel selects the top a.topk_k slots of each row itself: outputs idx/score
+// [B, sel_T, topk_k] (score nullable), counts cnt [B, sel_T] (nullable); rows of up to est_len
+// slots decide whether it keeps candidate lists.
+void set_self_select(ScoreArgs& a, const idx_problem* p, int32_t* idx, float* score, int32_t* cnt, int sel_T,
+                     int64_t est_len) {
+  a.sel_idx = idx; a.sel_score = score; a.sel_cnt = cnt; a.sel_T = sel_T;
+  a.slot_off = (int)rstride(p->N + 64);
+  // candidate lists pay off on long rows (the row's read-back shrinks to the list, for some
+  // extra work per tile)
+  a.sel_list = est_len > 32768 ? 1 : 0;
+}
+
+// proxy rows per scan chunk: the dense budget, in whole multiples of 2048 rows when more do not fit
+int proxy_chunk(const idx_problem* p, int64_t stride, int NG) {
+  int64_t rows = std::max<int64_t>(1, (int64_t)kDenseBudget / std::max<int64_t>(1, (int64_t)p->B * stride * 4));
+  if (rows >= 2048 && rows < NG) rows = rows / 2048 * 2048;
+  return (int)std::min<int64_t>(NG, rows);
+}
+
 // score rows are held in chunks of at most `row_budget` bytes
 DensePlan plan_dense(const idx_problem* p, void* ws, size_t row_budget = kDenseBudget) {
   DensePlan d;
   Carver c(ws);
   d.self_select = dense_self_select(p);
-  d.stride = d.self_select ? rstride(p->N + 64) + rstride(p->N + 64) / 2 : rstride(p->N);
+  d.stride = self_select_stride(p);
   int64_t rows = std::max<int64_t>(1, (int64_t)row_budget / std::max<int64_t>(1, (int64_t)p->B * d.stride * 4));
   // whole multiples of 2048 queries (256 work-groups of 8) when that many fit, so that each
   // launch fills the compute units evenly
@@ -162,6 +186,7 @@ DensePlan plan_dense(const idx_problem* p, void* ws, size_t row_budget = kDenseB
 
 struct ReusePlan {
   int NG, chunkP;
+  int64_t pstride;     // floats per proxy score row
   void* pq;
   float* pw;
   int32_t* ppos;
@@ -264,6 +289,7 @@ struct RefinePlan {
 
 struct GroupPlan {
   int NG, chunkP, chunkG, Cs;
+  int64_t pstride;     // floats per proxy score row
   void* pq;
   float* pw;
   int32_t* ppos;
@@ -288,8 +314,9 @@ GroupPlan plan_group(const idx_problem* p, int G, int C, void* ws, int32_t* out_
   g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
   g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
   g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
-  g.chunkP = chunk_rows(p->B, rstride(p->N) * 4, g.NG);
-  g.pscores = c.take<float>((size_t)p->B * g.chunkP * rstride(p->N));
+  g.pstride = self_select_stride(p);
+  g.chunkP = proxy_chunk(p, g.pstride, g.NG);
+  g.pscores = c.take<float>((size_t)p->B * g.chunkP * g.pstride);
   g.cand = out_cand ? out_cand : c.take<int32_t>((size_t)p->B * g.NG * Ce);
   g.cand_cnt = c.take<int32_t>((size_t)p->B * g.NG);
   g.chunkG = chunk_rows(p->B, (int64_t)G * rstride(Ce) * 4, g.NG);
@@ -493,14 +520,10 @@ int score_topk_impl(const idx_problem* p, int32_t k, int32_t* out_idx, float* ou
     a.scores = pl.scores; a.score_stride = pl.stride; a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
     const bool self_select = pl.self_select;
-    if (self_select) {
-      a.sel_idx = out_idx; a.sel_score = out_score; a.sel_T = p->T;
-      a.slot_off = (int)rstride(p->N + 64);
-      // candidate lists pay off on long rows (the row's read-back shrinks to the list, for some
-      // extra work per tile); a prefill chunk's queries sit at the end of the cache, so the
-      // chunk's longest row is about N - T + c1 slots
-      a.sel_list = std::min<int64_t>(p->N, (int64_t)p->N - p->T + c1) > 32768 ? 1 : 0;
-    }
+    // a prefill chunk's queries sit at the end of the cache, so the chunk's longest row is about
+    // N - T + c1 slots
+    if (self_select)
+      set_self_select(a, p, out_idx, out_score, nullptr, p->T, std::min<int64_t>(p->N, (int64_t)p->N - p->T + c1));
     bool fused;
     if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s, self_select ? cu_count() : kTargetGroups))))
       return st;
@@ -570,11 +593,16 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
     ScoreArgs a = base_score_args(p);
     a.q = pl.pq; a.w = pl.pw; a.q_pos = pl.ppos; a.T = pl.NG;
     a.c0 = c0; a.c1 = c1;
-    a.scores = pl.pscores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
+    a.scores = pl.pscores; a.score_stride = pl.pstride; a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
+    // bf16 proxies over up to 65536 keys select their candidates in the score kernel (proxy
+    // prefixes span the cache)
+    const bool self = dense_self_select(p);
+    if (self) set_self_select(a, p, pl.cand, nullptr, pl.cand_cnt, pl.NG, p->N);
     bool fused;
-    if ((st = from_hip(run_score(a, p->N, Cs, pl.meta, &fused, s)))) return st;
-    TopkArgs t = topk_args(pl.pscores, rstride(p->N), pl.row_len, p->B * (c1 - c0), Cs, c1 - c0, pl.NG, c0,
+    if ((st = from_hip(run_score(a, p->N, Cs, pl.meta, &fused, s, self ? cu_count() : kTargetGroups)))) return st;
+    if (fused && self) continue;
+    TopkArgs t = topk_args(pl.pscores, pl.pstride, pl.row_len, p->B * (c1 - c0), Cs, c1 - c0, pl.NG, c0,
                            pl.cand, nullptr, Cs);
     t.out_count = pl.cand_cnt;
     t.row_meta = fused ? pl.meta : nullptr;
@@ -598,8 +626,9 @@ ReusePlan plan_reuse(const idx_problem* p, int G, int k, void* ws) {
   g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
   g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
   g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
-  g.chunkP = chunk_rows(p->B, rstride(p->N) * 4, g.NG);
-  g.pscores = c.take<float>((size_t)p->B * g.chunkP * rstride(p->N));
+  g.pstride = self_select_stride(p);
+  g.chunkP = proxy_chunk(p, g.pstride, g.NG);
+  g.pscores = c.take<float>((size_t)p->B * g.chunkP * g.pstride);
   g.gidx = c.take<int32_t>((size_t)p->B * g.NG * k);
   g.gsc = c.take<float>((size_t)p->B * g.NG * k);
   g.gcnt = c.take<int32_t>((size_t)p->B * g.NG);
@@ -631,11 +660,14 @@ int reuse_impl(const idx_problem* p, int32_t k, int32_t G, int32_t* out_idx, flo
     ScoreArgs a = base_score_args(p);
     a.q = pl.pq; a.w = pl.pw; a.q_pos = pl.ppos; a.T = pl.NG;
     a.c0 = c0; a.c1 = c1;
-    a.scores = pl.pscores; a.score_stride = rstride(p->N); a.row_len = pl.row_len;
+    a.scores = pl.pscores; a.score_stride = pl.pstride; a.row_len = pl.row_len;
     a.rows_per_seq = c1 - c0;
+    const bool self = dense_self_select(p);
+    if (self) set_self_select(a, p, pl.gidx, pl.gsc, pl.gcnt, pl.NG, p->N);
     bool fused;
-    if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s)))) return st;
-    TopkArgs t = topk_args(pl.pscores, rstride(p->N), pl.row_len, p->B * (c1 - c0), k, c1 - c0, pl.NG, c0,
+    if ((st = from_hip(run_score(a, p->N, k, pl.meta, &fused, s, self ? cu_count() : kTargetGroups)))) return st;
+    if (fused && self) continue;
+    TopkArgs t = topk_args(pl.pscores, pl.pstride, pl.row_len, p->B * (c1 - c0), k, c1 - c0, pl.NG, c0,
                            pl.gidx, pl.gsc, k);
     t.out_count = pl.gcnt;
     t.row_meta = fused ? pl.meta : nullptr;

@@ -44,6 +44,7 @@ struct ScoreArgs {
   // candidate list (scores from the row start, their slots there) instead of every slot
   int32_t* sel_idx; float* sel_score; int sel_T;
   int slot_off, sel_list;
+  int32_t* sel_cnt;                // optional [B, sel_T]: selections per row (min(topk_k, finite))
 };
 
 // Pick rows from per-row score arrays: the top-k slots of each row (a set; with a row summary

@@ -340,6 +340,7 @@ score_kernel(ScoreArgs a) {
       }
       if constexpr (!LISTM) {
         if (a.sel_idx != nullptr && a.digit_bits == 12) {
+          if (a.sel_cnt != nullptr && lane == 0) a.sel_cnt[(int64_t)b * a.sel_T + t] = 0;
           int32_t* oi = a.sel_idx + ((int64_t)b * a.sel_T + t) * a.topk_k;
           float* os = a.sel_score ? a.sel_score + ((int64_t)b * a.sel_T + t) * a.topk_k : nullptr;
           for (int p = lane; p < a.topk_k; p += 64) {
@@ -797,6 +798,8 @@ score_kernel(ScoreArgs a) {
     }
     if constexpr (!LISTM) {
       if (a.sel_idx != nullptr && bits == 12) {
+        if (a.sel_cnt != nullptr && lane == 0)
+          a.sel_cnt[(int64_t)b * a.sel_T + t] = (int32_t)min((uint32_t)a.topk_k, tot);
         // the wave's share of the key tiles (idle after the last tile) holds bin b1's keys
         constexpr int SLICE = 2 * G::TILE_BYTES / NW / 4;
         wave_select_row<SLICE < 2048 ? SLICE : 2048, CMP>(
