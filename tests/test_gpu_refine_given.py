@@ -109,3 +109,22 @@ def test_group_candidates_reproduce_group_path():
     rng = np.random.default_rng(44)
     check_rows(p, k, G, gc, None, ri, rs, [(0, int(x)) for x in [0, 15, 16, 4095] + list(rng.integers(0, 4096, 6))],
                "given-group")
+
+
+@pytest.mark.timeout(900)
+def test_given16k_full_size_sampled_rows():
+    # the benchmarked shape: a 16384-token prefill, groups of 16 queries sharing a bank of 4096
+    # tokens drawn from the group's prefix
+    spec = W.WORKLOADS["given16k"]
+    p = spec["gen"](0)
+    G, C, k = spec["group_size"], spec["n_cand"], spec["k"]
+    banks = W.make_banks(p, G, C, 0)
+    say("case given16k full size (L=16384, G=16, banks of 4096, k=2048)")
+    gi, gs = run_given(p, k, G, banks)
+    rng = np.random.default_rng(9)
+    rows = sorted(set([0, 15, 16, 2047, 2048, 8191, 16383] + list(rng.integers(0, 16384, 9))))
+    check_rows(p, k, G, banks, None, gi, gs, [(0, t) for t in rows], "given16k")
+    # every row holds min(k, its set size) tokens
+    for t in rows:
+        P = min(t + 1, int(p.k_len[0]))
+        assert (gi[0, t] >= 0).sum() == min(k, int(np.sum(np.unique(banks[0, t // G][banks[0, t // G] >= 0]) < P)))
