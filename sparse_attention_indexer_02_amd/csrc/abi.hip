@@ -184,20 +184,6 @@ DensePlan plan_dense(const idx_problem* p, void* ws, size_t row_budget = kDenseB
   return d;
 }
 
-struct ReusePlan {
-  int NG, chunkP;
-  int64_t pstride;     // floats per proxy score row
-  void* pq;
-  float* pw;
-  int32_t* ppos;
-  float* pscores;
-  int32_t* gidx;
-  float* gsc;
-  int32_t* gcnt;
-  int32_t* row_len;
-  int32_t* meta;
-  size_t bytes;
-};
 
 int cu_count();
 
@@ -258,6 +244,35 @@ int log2i(int v) {
   return r;
 }
 
+// Decode-shaped groups (a few proxies per sequence over a long cache, e.g. the queries of one
+// multi-token-prediction step) scan with the decode kernels: the proxies' top entries come from
+// the decode scan and select instead of the prefill score kernel.
+bool proxy_by_decode(const idx_problem* p, int NG) {
+  return decode_supported(p->q_dtype, p->k_dtype, p->H, p->D, NG, p->N);
+}
+
+idx_problem proxy_problem(const idx_problem* p, int NG, const void* pq, const float* pw, const int32_t* ppos) {
+  idx_problem pp = *p;
+  pp.T = NG; pp.q = pq; pp.w = pw; pp.q_pos = ppos; pp.q_scale = nullptr;
+  return pp;
+}
+
+struct ReusePlan {
+  int NG, chunkP;
+  int64_t pstride;     // floats per proxy score row
+  bool pdec;           // the proxies' scan is the decode scan
+  DecodePlan dp;
+  void* pq;
+  float* pw;
+  int32_t* ppos;
+  float* pscores;
+  int32_t* gidx;
+  float* gsc;
+  int32_t* gcnt;
+  int32_t* row_len;
+  int32_t* meta;
+  size_t bytes;
+};
 struct GroupBlockPlan {
   int NG, NB, chunkP, chunkG;
   bool dec;            // members refine by the decode scan over the group's kept blocks
@@ -290,6 +305,8 @@ struct RefinePlan {
 struct GroupPlan {
   int NG, chunkP, chunkG, Cs;
   int64_t pstride;     // floats per proxy score row
+  bool pdec;           // the proxies' scan is the decode scan
+  DecodePlan dp;
   void* pq;
   float* pw;
   int32_t* ppos;
@@ -314,9 +331,16 @@ GroupPlan plan_group(const idx_problem* p, int G, int C, void* ws, int32_t* out_
   g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
   g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
   g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
-  g.pstride = self_select_stride(p);
-  g.chunkP = proxy_chunk(p, g.pstride, g.NG);
-  g.pscores = c.take<float>((size_t)p->B * g.chunkP * g.pstride);
+  g.pdec = proxy_by_decode(p, g.NG);
+  if (g.pdec) {
+    const idx_problem pp = proxy_problem(p, g.NG, nullptr, nullptr, nullptr);
+    carve_decode(g.dp, c, &pp, p->N, 2);
+    g.pstride = 0; g.chunkP = g.NG; g.pscores = nullptr;
+  } else {
+    g.pstride = self_select_stride(p);
+    g.chunkP = proxy_chunk(p, g.pstride, g.NG);
+    g.pscores = c.take<float>((size_t)p->B * g.chunkP * g.pstride);
+  }
   g.cand = out_cand ? out_cand : c.take<int32_t>((size_t)p->B * g.NG * Ce);
   g.cand_cnt = c.take<int32_t>((size_t)p->B * g.NG);
   g.chunkG = chunk_rows(p->B, (int64_t)G * rstride(Ce) * 4, g.NG);
@@ -588,7 +612,13 @@ int group_impl(const idx_problem* p, int32_t k, int32_t G, int32_t C, int32_t* o
   if ((st = from_hip(timed("proxy", s, [&] { return launch_proxy(pa, s); })))) return st;
 
   // proxy scans and candidate sets
-  for (int c0 = 0; c0 < pl.NG; c0 += pl.chunkP) {
+  if (pl.pdec) {
+    const idx_problem pp = proxy_problem(p, pl.NG, pl.pq, pl.pw, pl.ppos);
+    DecodeArgs a = decode_args(&pp, pl.dp, Cs, pl.cand, nullptr);
+    a.out_cnt = pl.cand_cnt;
+    if ((st = run_decode(a, s))) return st;
+  }
+  for (int c0 = 0; c0 < (pl.pdec ? 0 : pl.NG); c0 += pl.chunkP) {
     const int c1 = std::min(pl.NG, c0 + pl.chunkP);
     ScoreArgs a = base_score_args(p);
     a.q = pl.pq; a.w = pl.pw; a.q_pos = pl.ppos; a.T = pl.NG;
@@ -626,9 +656,16 @@ ReusePlan plan_reuse(const idx_problem* p, int G, int k, void* ws) {
   g.pq = c.take<uint8_t>((size_t)p->B * g.NG * p->H * p->D * qeb);
   g.pw = c.take<float>((size_t)p->B * g.NG * p->H);
   g.ppos = c.take<int32_t>((size_t)p->B * g.NG);
-  g.pstride = self_select_stride(p);
-  g.chunkP = proxy_chunk(p, g.pstride, g.NG);
-  g.pscores = c.take<float>((size_t)p->B * g.chunkP * g.pstride);
+  g.pdec = proxy_by_decode(p, g.NG);
+  if (g.pdec) {
+    const idx_problem pp = proxy_problem(p, g.NG, nullptr, nullptr, nullptr);
+    carve_decode(g.dp, c, &pp, p->N, 2);
+    g.pstride = 0; g.chunkP = g.NG; g.pscores = nullptr;
+  } else {
+    g.pstride = self_select_stride(p);
+    g.chunkP = proxy_chunk(p, g.pstride, g.NG);
+    g.pscores = c.take<float>((size_t)p->B * g.chunkP * g.pstride);
+  }
   g.gidx = c.take<int32_t>((size_t)p->B * g.NG * k);
   g.gsc = c.take<float>((size_t)p->B * g.NG * k);
   g.gcnt = c.take<int32_t>((size_t)p->B * g.NG);
@@ -655,7 +692,13 @@ int reuse_impl(const idx_problem* p, int32_t k, int32_t G, int32_t* out_idx, flo
   pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.D = p->D; pa.G = G; pa.n_groups = pl.NG;
   pa.pq = pl.pq; pa.pw = pl.pw; pa.ppos = pl.ppos;
   if ((st = from_hip(timed("proxy", s, [&] { return launch_proxy(pa, s); })))) return st;
-  for (int c0 = 0; c0 < pl.NG; c0 += pl.chunkP) {
+  if (pl.pdec) {
+    const idx_problem pp = proxy_problem(p, pl.NG, pl.pq, pl.pw, pl.ppos);
+    DecodeArgs a = decode_args(&pp, pl.dp, k, pl.gidx, pl.gsc);
+    a.out_cnt = pl.gcnt;
+    if ((st = run_decode(a, s))) return st;
+  }
+  for (int c0 = 0; c0 < (pl.pdec ? 0 : pl.NG); c0 += pl.chunkP) {
     const int c1 = std::min(pl.NG, c0 + pl.chunkP);
     ScoreArgs a = base_score_args(p);
     a.q = pl.pq; a.w = pl.pw; a.q_pos = pl.ppos; a.T = pl.NG;

@@ -65,7 +65,8 @@ __device__ __forceinline__ int frag_d0(int s, int g) {
 }
 
 
-template <int D, int HB, int KST, int PF, bool BLK>
+// NQ: queries per work-group in the block loop (1 when every work-group scans for one query)
+template <int D, int HB, int KST, int PF, bool BLK, int NQ>
 __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a) {
   constexpr int NS = D / 32;                      // K=32 MFMA steps
   constexpr int KEB = KST == DT_FP8 ? 1 : 2;      // key bytes per element
@@ -135,10 +136,10 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
   // query fragments and head weights of both queries (a lone query is repeated): all loads
   // first, then the fragments move to the accumulation registers (they are only MFMA operands
   // there, which leaves the vector registers to the key stream and the epilogue)
-  bf16x8_t qf[2][HB][NS];
-  float wv[2][HB][4];
+  bf16x8_t qf[NQ][HB][NS];
+  float wv[NQ][HB][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NQ; ++j) {
     const int64_t rr = j == 0 ? r0 : r1;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -164,7 +165,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NQ; ++j)
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -231,11 +232,11 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    f32x4v_t acc[2][2][HB];                                        // [set][query][head block]
+    f32x4v_t acc[2][NQ][HB];                                       // [set][query][head block]
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NQ; ++j)
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) acc[x][j][hb] = f32x4v_t{};
 
@@ -244,43 +245,43 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     // between MFMAs). Pieces 0 .. NE-1: ReLU and head weight of one accumulator element (query
     // q, head block hb, row r), in the order the MFMAs produced them; then the head sum over the
     // 4 lane groups, the scale, the LDS store and the histogram.
-    constexpr int NE = 2 * HB * 4;
+    constexpr int NE = NQ * HB * 4;
     constexpr int NPIECE = NE + 4;
     struct Epi {
-      float p[2][4];
-      float x[2];
+      float p[NQ][4];
+      float x[NQ];
     };
-    auto piece = [&](int k, Epi& st, int i, const f32x4v_t (&ac)[2][HB], float sc) {
+    auto piece = [&](int k, Epi& st, int i, const f32x4v_t (&ac)[NQ][HB], float sc) {
       if (k < NE) {
-        const int q = k & 1, hb = (k >> 1) % HB, r = k / (2 * HB);
+        const int q = k % NQ, hb = (k / NQ) % HB, r = k / (NQ * HB);
         const float t = __int_as_float(max(__float_as_int(ac[q][hb][r]), 0));
         st.p[q][r] = hb == 0 ? wv[q][hb][r] * t : fmaf(wv[q][hb][r], t, st.p[q][r]);
       } else if (k == NE) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) st.x[q] = (st.p[q][0] + st.p[q][1]) + (st.p[q][2] + st.p[q][3]);
+        for (int q = 0; q < NQ; ++q) st.x[q] = (st.p[q][0] + st.p[q][1]) + (st.p[q][2] + st.p[q][3]);
       } else if (k == NE + 1) {
         // sum of both swap outputs: the pair's total in every lane, whichever way it swaps
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NQ; ++q) {
           const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(st.x[q]), __float_as_uint(st.x[q]), false, false);
           st.x[q] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
         }
       } else if (k == NE + 2) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NQ; ++q) {
           const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.x[q]), __float_as_uint(st.x[q]), false, false);
           st.x[q] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
         }
       } else {
         // branch-free (a branch would end the interleave): masked lanes write to their own sink
         // words; a block before the first (i = -1) has a negative offset
-        const float v = (g == 1 ? st.x[1] : st.x[0]) * sc;
+        const float v = ((NQ == 2 && g == 1) ? st.x[NQ - 1] : st.x[0]) * sc;
         const int jl = (i * DC_WAVES + wave) * DC_KB + n;             // offset in the sub-chunk
         const bool valid = owner & ((unsigned)jl < (unsigned)(sub1 - sub0));
         *(valid ? my_ssc + jl : sink_f) = v;
       }
     };
-    auto epilogue = [&](int i, const f32x4v_t (&ac)[2][HB], float sc) {
+    auto epilogue = [&](int i, const f32x4v_t (&ac)[NQ][HB], float sc) {
       Epi st;
 #pragma unroll
       for (int k = 0; k < NPIECE; ++k) piece(k, st, i, ac, sc);
@@ -300,7 +301,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
       }
     };
 
-    constexpr int NM = 2 * HB * NS;                                 // MFMAs per block
+    constexpr int NM = NQ * HB * NS;                                // MFMAs per block
     for (int i0 = 0; i0 < iters; i0 += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
@@ -318,10 +319,10 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
         // i - 1 from set x ^ 1
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
-          const int s = t / (2 * HB), hb = (t >> 1) % HB, q = t & 1;
+          const int s = t / (NQ * HB), hb = (t / NQ) % HB, q = t % NQ;
           acc[x][q][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[q][hb][s], bfr[s], s == 0 ? f32x4v_t{} : acc[x][q][hb], 0, 0, 0);
-          if (t % (2 * HB) == 0 && s + 1 < NS) bfr[s + 1] = convert(raw[u], s + 1);
-          if (t == (NS - 2) * 2 * HB) {
+          if (t % (NQ * HB) == 0 && s + 1 < NS) bfr[s + 1] = convert(raw[u], s + 1);
+          if (t == (NS - 2) * NQ * HB) {
             if constexpr (BLK) {
               ktok[u] = ntok;
               issue_keys_at(ntok, raw[u]);
@@ -912,6 +913,7 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
       }
     }
   }
+  if (a.out_cnt != nullptr && tid == 0) a.out_cnt[r] = (int32_t)kk;
   for (int p = (int)kk + tid; p < a.k; p += RS_THREADS) {
     oidx[p] = -1;
     if (osc) osc[p] = -INFINITY;
@@ -937,7 +939,13 @@ size_t decode_scan_lds(int sub, int keep) {
 template <int D, int HB, int KST>
 static hipError_t launch_scan(const DecodeArgs& a, hipStream_t s) {
   const bool blk = a.blocks != nullptr;
-  auto kfn = blk ? decode_scan_kernel<D, HB, KST, dc_pf<KST>(), true> : decode_scan_kernel<D, HB, KST, dc_pf<KST>(), false>;
+  // one query per work-group (pairs of one, or a single query per sequence): half the MFMAs and
+  // epilogue per key block
+  const bool one = a.pair == 1 || a.T == 1;
+  auto kfn = blk ? (one ? decode_scan_kernel<D, HB, KST, dc_pf<KST>(), true, 1>
+                        : decode_scan_kernel<D, HB, KST, dc_pf<KST>(), true, 2>)
+                 : (one ? decode_scan_kernel<D, HB, KST, dc_pf<KST>(), false, 1>
+                        : decode_scan_kernel<D, HB, KST, dc_pf<KST>(), false, 2>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)decode_scan_lds(DC_SUB, blk ? DECODE_KEEP_MAX : 0));

@@ -122,6 +122,7 @@ struct DecodeArgs {
   int cand_cap;                    // >= N, multiple of 64
   int k;                           // selection size
   int32_t* out_idx; float* out_score;                        // [B, T, k]
+  int32_t* out_cnt;                // optional [B*T]: selections per row (the select writes it)
   int pair;                        // queries per scan work-group: 2, or 1 where a pair would span
                                    // two kept-block lists
   int vn;                          // slots per row: N, or keep_stride << blk_shift with blocks

@@ -105,3 +105,20 @@ def test_reuse64k_full_size_sampled_groups():
     rng = np.random.default_rng(4)
     groups = sorted(set([0, 127, 128, 2047, 4095] + list(rng.integers(0, 4096, 4))))
     check_reuse(p, k, G, gi, gs, "reuse64k", groups=[(0, g) for g in groups])
+
+
+@pytest.mark.timeout(900)
+def test_decode_grouping_full_size_sampled_sequences():
+    # the benchmarked decode-grouping shapes: 32 sequences of 131072 FP8 keys, the 2 MTP queries of
+    # a step form one group (the proxies' scan is the decode scan); both variants
+    rs, gs_ = W.WORKLOADS["decodereuse128k"], W.WORKLOADS["decodegroup128k"]
+    p = rs["gen"](0)
+    G, k, C = rs["group_size"], rs["k"], gs_["n_cand"]
+    assert gs_["group_size"] == G and gs_["k"] == k
+    say("case decodereuse128k / decodegroup128k full size (B=32, N=131072, T=2, G=2, k=2048, C=8192)")
+    gi, gsc = run_reuse(p, k, G)
+    seqs = [0, 9, 31]
+    check_reuse(p, k, G, gi, gsc, "decodereuse128k", groups=[(b, 0) for b in seqs])
+    ri, rsc, rc = run_group(p, k, G, C)
+    check_group(p, k, G, C, ri, rsc, rc, [(b, 0) for b in seqs], "decodegroup128k")
+    assert ((ri >= 0).sum(-1) == k).all()

@@ -291,6 +291,11 @@ WORKLOADS = {
     "decodegblk128k": dict(op="gblock", k=2048, group_size=2, block_size=128, n_blocks_keep=128,
                            pooled=True,
                            gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed, n_regions=64)),
+    # decode-phase grouping (a step's 2 MTP queries form one group, PIVOT) on decode128k's inputs
+    "decodegroup128k": dict(op="group", k=2048, group_size=2, n_cand=8192,
+                            gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed)),
+    "decodereuse128k": dict(op="reuse", k=2048, group_size=2,
+                            gen=lambda seed=0: make_decode(32, 131072, 2, seed=seed)),
     # a layer scoring a shared 64-dimensional latent cache through absorbed queries (D = 128):
     # a 64K prefill (bf16 latent) and a 128K decode step (FP8 latent with per-token scales)
     "latent64k": dict(op="latent", k=2048,
