@@ -558,9 +558,9 @@ __device__ __forceinline__ void block_find_desc(const uint32_t* h, uint32_t need
 // slots first); then the padding.
 
 __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a) {
-  __shared__ __align__(16) uint32_t hist[DC_BINS];
-  __shared__ uint32_t ckey[RS_LDS_CAND];
-  __shared__ uint32_t cpos[RS_LDS_CAND];
+  __shared__ __align__(16) uint32_t hist[DC_BINS + 128];       // + per-lane sink words (staging)
+  __shared__ uint32_t ckey[RS_LDS_CAND + 64];                     // + per-lane sink entries
+  __shared__ uint32_t cpos[RS_LDS_CAND + 64];
   __shared__ uint32_t sh[RS_WAVES];
   __shared__ uint32_t wsum[2 * RS_WAVES];
   __shared__ __align__(16) uint32_t cbase[RS_R];
@@ -704,25 +704,39 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
         clim[u] = 0;
       }
     }
-    if (lane == 0) bc[6] = fits ? 1u : 0u;
+    if (lane == 0) {
+      bc[6] = fits ? 1u : 0u;
+      bc[7] = tot;                                         // chunks in use
+    }
   }
   __syncthreads();
   const bool held = kk > 0 && bc[6] != 0u;
+  // the held path's selections above b1 (fewer than kk) are staged in the histogram's LDS (free
+  // until the bin-b1 passes) and written out together: stores into global memory inside its loop
+  // made every iteration wait for the previous ones
+  const bool stage = held && kk <= (uint32_t)(DC_BINS / 2);
   if (held) {
-    // keys; 0 (below every finite score's key) where a chunk has no candidate
+    // keys; 0 (below every finite score's key) where a chunk has no candidate. The loops stop
+    // at the chunks in use (a uniform bound; the register arrays stay statically indexed)
+    const int nchk = (int)bc[7];
     uint32_t xr[RS_R], ir[RS_R];                           // key and slot
 #pragma unroll
-    for (int u = 0; u < RS_R; u += 4) {
-      const u32x4_t cb = *reinterpret_cast<const u32x4_t*>(cbase + u);
-      const int4 cl = *reinterpret_cast<const int4*>(clim + u);
-      const int lim[4] = {cl.x, cl.y, cl.z, cl.w};
+    for (int u = 0; u < RS_R; ++u) {
+      xr[u] = 0u;
+      ir[u] = 0u;
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xr[u + e] = 0u;
-        ir[u + e] = 0u;
-        if (tid < lim[e]) {
-          xr[u + e] = gk[cb[e] + (uint32_t)tid];
-          ir[u + e] = gi[cb[e] + (uint32_t)tid];
+    for (int u = 0; u < RS_R; u += 4) {
+      if (u < nchk) {
+        const u32x4_t cb = *reinterpret_cast<const u32x4_t*>(cbase + u);
+        const int4 cl = *reinterpret_cast<const int4*>(clim + u);
+        const int lim[4] = {cl.x, cl.y, cl.z, cl.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (tid < lim[e]) {
+            xr[u + e] = gk[cb[e] + (uint32_t)tid];
+            ir[u + e] = gi[cb[e] + (uint32_t)tid];
+          }
         }
       }
     }
@@ -733,9 +747,12 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
     uint32_t cs = 0, cq = 0;                               // this lane's counts
 #pragma unroll
     for (int u = 0; u < RS_R; ++u) {
-      cs += is_sel(xr[u], b1) ? 1u : 0u;
-      cq += is_cand(xr[u], b1) ? 1u : 0u;
+      if (u < nchk) {
+        cs += is_sel(xr[u], b1) ? 1u : 0u;
+        cq += is_cand(xr[u], b1) ? 1u : 0u;
+      }
     }
+    const uint32_t cs_own = cs, cq_own = cq;
     cs = wave_scan_dpp(cs);
     cq = wave_scan_dpp(cq);
     if (lane == 63) {
@@ -764,8 +781,32 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
     asm volatile("" : "+v"(b1x));
 #pragma unroll
     for (int u = 0; u < RS_R; ++u) asm volatile("" : "+v"(xr[u]));
+    if (stage) {
+      // lane order instead of chunk order: each lane writes its own entries from its offset (the
+      // exclusive scan of the counts above), without ballots, without branches (an entry a lane
+      // does not keep goes to its own sink words)
+      uint32_t ls = ps + cs - cs_own, lc = pc + cq - cq_own;
+#pragma unroll
+      for (int u = 0; u < RS_R; ++u) {
+        if (u >= nchk) continue;
+        const bool sel = is_sel(xr[u], b1x), cand = is_cand(xr[u], b1x);
+        const uint32_t at = (sel && ls < (uint32_t)(DC_BINS / 2)) ? 2u * ls : (uint32_t)DC_BINS + 2u * (uint32_t)lane;
+        hist[at] = ir[u];
+        hist[at + 1] = xr[u];
+        const uint32_t cl = (cand && lc < (uint32_t)RS_LDS_CAND) ? lc : (uint32_t)RS_LDS_CAND + (uint32_t)lane;
+        ckey[cl] = xr[u];
+        cpos[cl] = ir[u];
+        if (cand && lc >= (uint32_t)RS_LDS_CAND) {
+          g2k[lc] = xr[u];
+          g2p[lc] = ir[u];
+        }
+        ls += sel ? 1u : 0u;
+        lc += cand ? 1u : 0u;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < RS_R; ++u) {
+      if (stage || u >= nchk) continue;
       const bool sel = is_sel(xr[u], b1x), cand = is_cand(xr[u], b1x);
       const uint64_t ms = __ballot(sel), mc = __ballot(cand);
       const uint32_t sl = ir[u];
@@ -830,6 +871,14 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
     }, std::true_type{});
   }
   __syncthreads();
+  if (stage) {
+    for (uint32_t i = tid; i < min(bc[4], (uint32_t)(DC_BINS / 2)); i += RS_THREADS) {
+      const uint32_t sl = hist[2 * i], x = hist[2 * i + 1];
+      oidx[i] = tok(sl);
+      if (osc) osc[i] = key2f(x);
+    }
+    __syncthreads();
+  }
 
   if (kk > 0 && !all) {
     const uint32_t nc = bc[5];
