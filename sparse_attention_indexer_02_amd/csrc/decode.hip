@@ -43,8 +43,9 @@ constexpr int DC_THREADS = DC_WAVES * 64;
 constexpr int DC_BINS = DECODE_BINS;             // 12-bit first digit
 constexpr int DC_KB = 16;                        // keys per block (MFMA columns)
 constexpr int DC_SUB = DECODE_SUB;               // keys per sub-chunk held in LDS
-// blocks in flight per wave (FP8 keys: 2 KB per block per wave; bf16 keys: 4 KB)
-template <int KST> constexpr int dc_pf() { return KST == DT_FP8 ? 8 : 4; }
+// blocks in flight per wave (FP8 keys: 2 KB per block per wave; bf16 keys: 4 KB), 8 per SIMD
+template <int KST, int W> constexpr int dc_pf() { return (KST == DT_FP8 ? 8 : 4) * 4 / W; }
+constexpr int DC_SCAN_WAVES = 4;                 // scan work-group: waves per work-group
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v_t;
 
@@ -52,6 +53,12 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v_t;
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// f2key in three operations (shift, or, xor): the sign bit selects complement or top bit
+__device__ __forceinline__ uint32_t f2key3(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return u ^ (uint32_t)((int32_t)u >> 31 | (int32_t)0x80000000);
 }
 
 // Element placement (the same permutation of d is used for queries and keys, so dot products
@@ -65,16 +72,20 @@ __device__ __forceinline__ int frag_d0(int s, int g) {
 }
 
 
-// NQ: queries per work-group in the block loop (1 when every work-group scans for one query)
-template <int D, int HB, int KST, int PF, bool BLK, int NQ>
-__global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a) {
+// NQ: queries per work-group in the block loop (1 when every work-group scans for one query);
+// W: waves per work-group (4: one per SIMD; 8: two per SIMD, a wave's MFMAs beside the other's
+// vector work)
+template <int D, int HB, int KST, int PF, bool BLK, int NQ, int W>
+__global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
+  constexpr int NW = W, NT = W * 64;
   constexpr int NS = D / 32;                      // K=32 MFMA steps
   constexpr int KEB = KST == DT_FP8 ? 1 : 2;      // key bytes per element
   constexpr int NLD = D * KEB / 64;               // 16-byte loads per lane per block
   static_assert(PF % 2 == 0, "blocks alternate between two accumulator sets");
   extern __shared__ __align__(16) uint8_t lds[];
-  float* ssc = reinterpret_cast<float*>(lds);                      // [2][sub] scores
-  uint32_t* hist = reinterpret_cast<uint32_t*>(lds + 8 * a.sub);   // [2][2048] 16-bit bins
+  // scores [2][sub] (an area of 2 DC_SUB, so that a row's reads of DC_SUB slots stay inside it)
+  float* ssc = reinterpret_cast<float*>(lds);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(lds + 8 * DC_SUB);  // [2][2048] 16-bit bins
   uint32_t* misc = hist + 2 * 2048;                                // [32]
   uint32_t* sink = misc + 32;                                      // [2][64] per-lane sinks
   int32_t* btab = reinterpret_cast<int32_t*>(sink + 128);          // BLK: [keep_stride] kept blocks
@@ -97,7 +108,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     const int nk = max(0, min(a.n_kept[lrow], a.keep_stride));
     const int bsz = 1 << a.blk_shift;
     uint32_t s0 = 0, s1 = 0;
-    for (int j = tid; j < nk; j += DC_THREADS) {
+    for (int j = tid; j < nk; j += NT) {
       const int blk = a.blocks[lrow * a.keep_stride + j];
       btab[j] = blk;
       const int base = blk << a.blk_shift;
@@ -113,7 +124,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     __syncthreads();
     V0 = V1 = 0;
 #pragma unroll
-    for (int w = 0; w < DC_WAVES; ++w) {
+    for (int w = 0; w < NW; ++w) {
       V0 += (int)misc[w];
       V1 += (int)misc[8 + w];
     }
@@ -126,7 +137,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     // sub-chunks of this chunk past the causal limit have no candidates
     const int s_lo = c0 >= c1 ? c0 / a.sub : (c1 + a.sub - 1) / a.sub;
     const int s_hi = min(c0 + a.chunk, a.vn);
-    for (int sg = s_lo + tid; sg * a.sub < s_hi; sg += DC_THREADS) {
+    for (int sg = s_lo + tid; sg * a.sub < s_hi; sg += NT) {
       a.ccount[r0 * a.nsegs + sg] = 0u;
       if (two) a.ccount[r1 * a.nsegs + sg] = 0u;
     }
@@ -182,12 +193,13 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
 
   for (int sub0 = c0; sub0 < c1; sub0 += a.sub) {
     const int sub1 = min(sub0 + a.sub, c1);
-    for (int i = tid; i < 2 * 2048; i += DC_THREADS) hist[i] = 0u;
+    for (int i = tid; i < 2 * 2048; i += NT) hist[i] = 0u;
+    if (tid < 2) misc[12 + tid] = 0u;                               // candidates written
     __syncthreads();
 
     // ---- scores of the sub-chunk into LDS
     const int nblk = (sub1 - sub0 + DC_KB - 1) / DC_KB;
-    const int per_wave = (nblk + DC_WAVES - 1) / DC_WAVES;
+    const int per_wave = (nblk + NW - 1) / NW;
     const int iters = (per_wave + PF - 1) / PF * PF;               // extra blocks are masked
     // slot u of raw holds the bytes of a block from its issue until its MFMAs; slot u of scl
     // holds a block's scale until its epilogue, one slot later, so that no loaded register is
@@ -197,7 +209,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     // token of lane n's key in block i (clamped: always issued; with kept blocks, slot -> token
     // through the LDS table, the same entry for a whole 16-key block)
     auto key_of = [&](int i) {
-      const int blk = min(i * DC_WAVES + wave, nblk - 1);
+      const int blk = min(i * NW + wave, nblk - 1);
       int v = sub0 + blk * DC_KB + n;
       if constexpr (BLK) {
         v = min(v, vmax - 1);
@@ -227,7 +239,8 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
       const int up = (u + PF - 1) % PF;
       ktok[u] = key_of(u);
       issue_keys_at(ktok[u], raw[u]);
-      if constexpr (BLK) issue_scale_at(ktok[u == 0 ? 0 : up], scl[up]);
+      if constexpr (W == 8) issue_scale_at(ktok[u], scl[u]);
+      else if constexpr (BLK) issue_scale_at(ktok[u == 0 ? 0 : up], scl[up]);
       else issue_scale_at(key_of(up), scl[up]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -276,7 +289,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
         // branch-free (a branch would end the interleave): masked lanes write to their own sink
         // words; a block before the first (i = -1) has a negative offset
         const float v = ((NQ == 2 && g == 1) ? st.x[NQ - 1] : st.x[0]) * sc;
-        const int jl = (i * DC_WAVES + wave) * DC_KB + n;             // offset in the sub-chunk
+        const int jl = (i * NW + wave) * DC_KB + n;             // offset in the sub-chunk
         const bool valid = owner & ((unsigned)jl < (unsigned)(sub1 - sub0));
         *(valid ? my_ssc + jl : sink_f) = v;
       }
@@ -302,6 +315,64 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     };
 
     constexpr int NM = NQ * HB * NS;                                // MFMAs per block
+    if constexpr (W == 8) {
+      // Two waves per SIMD: one wave's MFMAs run beside the other's vector work, so a block is
+      // scored in program order (convert, MFMAs, epilogue) and its head blocks are pipelined
+      // (the MFMAs of head block hb + 1 are issued before the ReLU and weights of hb).
+      for (int i0 = 0; i0 < iters; i0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          const int i = i0 + u;
+          int ntok = 0;
+          if constexpr (BLK) ntok = key_of(i + PF);
+          bf16x8_t bfr[NS];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) bfr[s] = convert(raw[u], s);
+          // the slot's keys are converted: refill it with block i + PF
+          if constexpr (BLK) {
+            ktok[u] = ntok;
+            issue_keys_at(ntok, raw[u]);
+          } else {
+            issue_keys_at(key_of(i + PF), raw[u]);
+          }
+          float p[NQ][4];
+          f32x4v_t ac[2][NQ];
+          auto mm = [&](int hb, f32x4v_t (&o)[NQ]) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int q = 0; q < NQ; ++q)
+                o[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[q][hb][s], bfr[s], s == 0 ? f32x4v_t{} : o[q], 0, 0, 0);
+          };
+          auto ep = [&](int hb, const f32x4v_t (&o)[NQ]) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int q = 0; q < NQ; ++q) {
+                const float t = __int_as_float(max(__float_as_int(o[q][r]), 0));
+                p[q][r] = hb == 0 ? wv[q][hb][r] * t : fmaf(wv[q][hb][r], t, p[q][r]);
+              }
+          };
+          mm(0, ac[0]);
+#pragma unroll
+          for (int hb = 1; hb < HB; ++hb) {
+            mm(hb, ac[hb & 1]);
+            ep(hb - 1, ac[(hb - 1) & 1]);
+          }
+          ep(HB - 1, ac[(HB - 1) & 1]);
+          Epi st;
+#pragma unroll
+          for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.p[q][r] = p[q][r];
+#pragma unroll
+          for (int k = NE; k < NPIECE; ++k) piece(k, st, i, acc[0], scl[u]);   // (no accumulator read)
+          // the slot's scale is used: refill it with block i + PF's
+          if constexpr (BLK) issue_scale_at(ktok[u], scl[u]);
+          else issue_scale_at(key_of(i + PF), scl[u]);
+        }
+      }
+    } else {
     for (int i0 = 0; i0 < iters; i0 += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
@@ -339,21 +410,56 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
       }
     }
     epilogue(iters - 1, acc[1], scl[PF - 1]);                      // iters is a multiple of even PF
+    }
     __syncthreads();
 
-    // ---- first-digit histogram of each row's scores in the sub-chunk (its visible keys), from
-    // LDS after the block loop: kept out of the loop, whose VALU issue is the bottleneck
+    // ---- the sub-chunk's scores of row qq as order-preserving keys in registers, half a row at a
+    // time: thread tid takes slots j = 1024 st + 4 tid + e (0, below every score's key, past the
+    // row's visible slots; loads past them stay inside the score area)
+    constexpr int MST = DC_SUB / (4 * NT), HST = MST / 2;
+    const int len = sub1 - sub0;
+    auto load_keys = [&](int qq, int h, uint32_t (&kr)[HST][4]) {
+      int lim = min(len, (qq ? V1 : V0) - sub0);                   // visible slots
+      asm volatile("" : "+s"(lim));       // the masks are recomputed per call, not kept (64 pairs)
+      const float* row = ssc + qq * a.sub + 4 * tid;
+      f32x4_t v[HST];
+#pragma unroll
+      for (int u = 0; u < HST; ++u) v[u] = *reinterpret_cast<const f32x4_t*>(row + (h * HST + u) * 4 * NT);
+      __builtin_amdgcn_sched_barrier(0);         // the loads in flight together
+      if (lim >= MST * 4 * NT) {                           // every slot visible
+#pragma unroll
+        for (int u = 0; u < HST; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kr[u][e] = f2key3(v[u][e]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < HST; ++u) {
+          const int j = (h * HST + u) * 4 * NT + 4 * tid;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kr[u][e] = j + e < lim ? f2key3(v[u][e]) : 0u;
+          __builtin_amdgcn_sched_barrier(0);     // a few compare masks live at a time, not 32
+        }
+      }
+    };
+    // first-digit histogram of each row's visible finite scores (kept out of the block loop,
+    // whose VALU issue is the bottleneck)
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       if (qq < nrows) {
-        const int lim = min(sub1, qq ? V1 : V0) - sub0;               // visible slots
         uint32_t* hq = hist + qq * 2048;
-        for (int j = 4 * tid; j < lim; j += 4 * DC_THREADS) {
-          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ssc + qq * a.sub + j);
+        uint32_t* hsink = sink + 64 + lane;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t key = f2key(v[e]);
-            if ((j + e < lim) & (key > KEY_NEG_INF)) atomicAdd(hq + ((key >> 20) & 2047u), 1u << ((key >> 31) * 16));
+        for (int h = 0; h < 2; ++h) {
+          uint32_t kr[HST][4];
+          load_keys(qq, h, kr);
+#pragma unroll
+          for (int u = 0; u < HST; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // branch-free: a hidden or -inf slot adds to the lane's own sink word
+              const uint32_t x = kr[u][e];
+              atomicAdd(x > KEY_NEG_INF ? hq + ((x >> 20) & 2047u) : hsink, 1u << ((x >> 27) & 16u));
+            }
           }
         }
       }
@@ -364,7 +470,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     // of both rows and finds the bin b of each row's k-th largest score in this sub-chunk (both
     // rows' counts packed in one word: each <= DC_SUB).
     // The keys in bins >= b are this sub-chunk's candidates.
-    constexpr int BPT = DC_BINS / DC_THREADS;                       // bins per thread
+    constexpr int BPT = DC_BINS / NT;                       // bins per thread
     static_assert(BPT % 8 == 0, "whole 16-byte reads of packed bins");
     uint32_t bins[2][BPT];
     uint32_t part = 0;
@@ -375,12 +481,13 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     for (int qq = 0; qq < 2; ++qq) {
       uint32_t sum = 0;
       // the selector sums the sub-chunks' histograms (every key in a bin at or above a
-      // sub-chunk's bound is one of its candidates); threads 0-127 hold every word once
+      // sub-chunk's bound is one of its candidates); the first half of the threads holds every
+      // word once
       uint32_t* hout = a.shist + ((qq ? r1 : r0) * a.nsegs + seg) * (DC_BINS / 2) + w0;
 #pragma unroll
       for (int c = 0; c < BPT / 4; ++c) {
         const u32x4_t w = *reinterpret_cast<const u32x4_t*>(hist + qq * 2048 + w0 + 4 * c);
-        if ((qq < nrows) & (tid < 128)) reinterpret_cast<u32x4_t*>(hout)[c] = w;
+        if ((qq < nrows) & (tid < NT / 2)) reinterpret_cast<u32x4_t*>(hout)[c] = w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           bins[qq][4 * c + e] = (w[e] >> hsh) & 0xFFFFu;
@@ -394,7 +501,7 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
     __syncthreads();
     uint32_t before = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < DC_WAVES; ++w) {
+    for (int w = 0; w < NW; ++w) {
       before += w < wave ? misc[16 + w] : 0u;
       total += misc[16 + w];
     }
@@ -425,85 +532,62 @@ __global__ void __launch_bounds__(DC_THREADS, 1) decode_scan_kernel(DecodeArgs a
       }
     }
     __syncthreads();
-    // the candidates of a sub-chunk go to the same slots of the row's candidate list (a key is a
-    // candidate of one sub-chunk only), and their count to the sub-chunk's counter
-    if (tid < nrows) a.ccount[(tid ? r1 : r0) * a.nsegs + sub0 / a.sub] = misc[4 * tid + 1];
-    // ---- candidates (order-preserving key, slot) at or above each row's bound. Wave w takes
-    // the slots j with (j / 256) % DC_WAVES == w, 4 per lane per step: a first pass counts them,
-    // the waves' counts are prefix-summed, a second pass compacts each step's candidates in the
-    // wave's LDS staging area (the histogram's, free again) and writes them as contiguous runs.
-    const int len = sub1 - sub0;
-    const int steps = (len + 4 * DC_THREADS - 1) / (4 * DC_THREADS);
-    auto sel_flags = [&](int qq, int st, uint32_t thr, uint32_t (&key)[4], bool (&f)[4]) {
-      const int j0 = st * 4 * DC_THREADS + wave * 256 + 4 * lane;
-      const int jr = min(j0, a.sub - 4);
-      const int lim = min(len, (qq ? V1 : V0) - sub0);
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ssc + qq * a.sub + jr);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[e] = f2key(v[e]);
-        f[e] = (j0 + e < lim) & (key[e] >= thr);
-      }
-    };
-    uint32_t wcnt[2] = {0u, 0u};
+    // ---- candidates (order-preserving key, slot) at or above each row's bound, written to the
+    // sub-chunk's own slots of the row's candidate list (a key is a candidate of one sub-chunk
+    // only) in any order: a wave reserves its run with one LDS atomic, then writes its entries
+    // one register at a time, the lanes that hold one at consecutive positions (ballot rank)
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       if (qq < nrows) {
-        const uint32_t thr = misc[4 * qq];
-        uint32_t c = 0;
-#pragma unroll 4
-        for (int st = 0; st < steps; ++st) {
-          uint32_t key[4];
-          bool f[4];
-          sel_flags(qq, st, thr, key, f);
+        // a candidate: a finite score's key at or above the bound (keys of hidden slots are 0)
+        const uint32_t thr = max(misc[4 * qq], KEY_NEG_INF + 1u);
+        uint32_t n = 0;                                              // the wave's count
 #pragma unroll
-          for (int e = 0; e < 4; ++e) c += f[e] ? 1u : 0u;
+        for (int h = 0; h < 2; ++h) {
+          uint32_t kr[HST][4];
+          load_keys(qq, h, kr);
+#pragma unroll
+          for (int u = 0; u < HST; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) n += (uint32_t)__popcll(__ballot(kr[u][e] >= thr));
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        wcnt[qq] = wave_bcast(wave_scan_dpp(c), 63);
-      }
-    }
-    if (lane == 0) {
-      misc[16 + wave] = wcnt[0];
-      misc[24 + wave] = wcnt[1];
-    }
-    __syncthreads();
-    uint32_t* stage_k = hist + wave * 512;                        // [256] keys, [256] slots
-    uint32_t* stage_i = stage_k + 256;
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      if (qq < nrows) {
-        const uint32_t thr = misc[4 * qq];
-        uint32_t pos = (uint32_t)sub0;
-        for (int w = 0; w < wave; ++w) pos += misc[16 + 8 * qq + w];
+        uint32_t pos = 0;
+        if (lane == 0 && n) pos = atomicAdd(&misc[12 + qq], n);
+        pos = (uint32_t)sub0 + wave_bcast(pos, 0);
         const int64_t rr = qq ? r1 : r0;
-        uint32_t* ck = a.cand_key + rr * a.cand_cap;
-        uint32_t* ci = a.cand_idx + rr * a.cand_cap;
-        for (int st = 0; st < steps; ++st) {
-          uint32_t key[4];
-          bool f[4];
-          sel_flags(qq, st, thr, key, f);
-          const uint32_t jb = (uint32_t)(sub0 + st * 4 * DC_THREADS + wave * 256 + 4 * lane);
-          const uint32_t c = (f[0] ? 1u : 0u) + (f[1] ? 1u : 0u) + (f[2] ? 1u : 0u) + (f[3] ? 1u : 0u);
-          const uint32_t inc = wave_scan_dpp(c);
-          const uint32_t n = wave_bcast(inc, 63);
-          uint32_t o = inc - c;                                  // this lane's first staging slot
+        // byte offsets below 2^32 from uniform bases (one row's list)
+        uint8_t* ck = reinterpret_cast<uint8_t*>(a.cand_key + rr * a.cand_cap);
+        uint8_t* ci = reinterpret_cast<uint8_t*>(a.cand_idx + rr * a.cand_cap);
+        const uint32_t slot0 = (uint32_t)(sub0 + 4 * tid);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (f[e]) {
-              stage_k[o] = key[e];
-              stage_i[o] = jb + e;
+        for (int h = 0; h < 2; ++h) {
+          uint32_t kr[HST][4];
+          load_keys(qq, h, kr);
+#pragma unroll
+          for (int u = 0; u < HST; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t x = kr[u][e];
+              const bool f = x >= thr;
+              const uint64_t m = __ballot(f);
+              if (f) {
+                const uint32_t at = 4u * (pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)));
+                *reinterpret_cast<uint32_t*>(ck + at) = x;
+                *reinterpret_cast<uint32_t*>(ci + at) = slot0 + (uint32_t)((h * HST + u) * 4 * NT + e);
+              }
+              pos += (uint32_t)__popcll(m);
+              __builtin_amdgcn_sched_barrier(0);                   // one register's masks live at a time
             }
-            o += f[e] ? 1u : 0u;
           }
-          for (uint32_t i = lane; i < n; i += 64) {
-            ck[pos + i] = stage_k[i];
-            ci[pos + i] = stage_i[i];
-          }
-          pos += n;
         }
       }
     }
     __syncthreads();
+    // the sub-chunk's candidate count (read by thread qq, the one that clears the row's counter
+    // at the next sub-chunk's start)
+    if (tid < nrows) a.ccount[(tid ? r1 : r0) * a.nsegs + seg] = misc[12 + tid];
   }
 }
 
@@ -981,26 +1065,25 @@ bool decode_blocks_supported(int q_dtype, int k_dtype, int H, int D, int T, int 
          (block_size & (block_size - 1)) == 0 && keep <= DECODE_KEEP_MAX;
 }
 
-size_t decode_scan_lds(int sub, int keep) {
-  return (size_t)8 * sub + 2 * 2048 * 4 + (32 + 128) * 4 + (size_t)4 * keep;
+size_t decode_scan_lds(int keep) {
+  return (size_t)8 * DC_SUB + 2 * 2048 * 4 + (32 + 128) * 4 + (size_t)4 * keep;
 }
 
 template <int D, int HB, int KST>
 static hipError_t launch_scan(const DecodeArgs& a, hipStream_t s) {
+  constexpr int W = DC_SCAN_WAVES, PF = dc_pf<KST, W>();
   const bool blk = a.blocks != nullptr;
   // one query per work-group (pairs of one, or a single query per sequence): half the MFMAs and
   // epilogue per key block
   const bool one = a.pair == 1 || a.T == 1;
-  auto kfn = blk ? (one ? decode_scan_kernel<D, HB, KST, dc_pf<KST>(), true, 1>
-                        : decode_scan_kernel<D, HB, KST, dc_pf<KST>(), true, 2>)
-                 : (one ? decode_scan_kernel<D, HB, KST, dc_pf<KST>(), false, 1>
-                        : decode_scan_kernel<D, HB, KST, dc_pf<KST>(), false, 2>);
+  auto kfn = blk ? (one ? decode_scan_kernel<D, HB, KST, PF, true, 1, W> : decode_scan_kernel<D, HB, KST, PF, true, 2, W>)
+                 : (one ? decode_scan_kernel<D, HB, KST, PF, false, 1, W> : decode_scan_kernel<D, HB, KST, PF, false, 2, W>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)decode_scan_lds(DC_SUB, blk ? DECODE_KEEP_MAX : 0));
+                                     (int)decode_scan_lds(blk ? DECODE_KEEP_MAX : 0));
   if (e != hipSuccess) return e;
   dim3 grid(a.B * a.nchunk, (a.T + a.pair - 1) / a.pair);
-  hipLaunchKernelGGL(kfn, grid, dim3(DC_THREADS), decode_scan_lds(a.sub, blk ? a.keep_stride : 0), s, a);
+  hipLaunchKernelGGL(kfn, grid, dim3(W * 64), decode_scan_lds(blk ? a.keep_stride : 0), s, a);
   return hipGetLastError();
 }
 
