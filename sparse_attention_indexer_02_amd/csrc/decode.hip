@@ -38,14 +38,13 @@
 
 namespace idx {
 
-constexpr int DC_WAVES = 4;                      // one per SIMD
-constexpr int DC_THREADS = DC_WAVES * 64;
 constexpr int DC_BINS = DECODE_BINS;             // 12-bit first digit
 constexpr int DC_KB = 16;                        // keys per block (MFMA columns)
 constexpr int DC_SUB = DECODE_SUB;               // keys per sub-chunk held in LDS
 // blocks in flight per wave (FP8 keys: 2 KB per block per wave; bf16 keys: 4 KB), 8 per SIMD
 template <int KST, int W> constexpr int dc_pf() { return (KST == DT_FP8 ? 8 : 4) * 4 / W; }
-constexpr int DC_SCAN_WAVES = 4;                 // scan work-group: waves per work-group
+// waves per scan work-group: one per SIMD at D = 128; two per SIMD at D = 64, where the query
+// fragments take half the registers and a second wave per SIMD measured 7-10% faster
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v_t;
 
@@ -260,35 +259,40 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
     // 4 lane groups, the scale, the LDS store and the histogram.
     constexpr int NE = NQ * HB * 4;
     constexpr int NPIECE = NE + 4;
+    // A lane's 16 heads of a query are summed in one chain (consecutive links of a chain are
+    // NQ pieces, at least one MFMA, apart).
     struct Epi {
-      float p[NQ][4];
+      float p[NQ];
       float x[NQ];
     };
     auto piece = [&](int k, Epi& st, int i, const f32x4v_t (&ac)[NQ][HB], float sc) {
       if (k < NE) {
         const int q = k % NQ, hb = (k / NQ) % HB, r = k / (NQ * HB);
         const float t = __int_as_float(max(__float_as_int(ac[q][hb][r]), 0));
-        st.p[q][r] = hb == 0 ? wv[q][hb][r] * t : fmaf(wv[q][hb][r], t, st.p[q][r]);
+        st.p[q] = k < NQ ? wv[q][hb][r] * t : fmaf(wv[q][hb][r], t, st.p[q]);
       } else if (k == NE) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) st.x[q] = (st.p[q][0] + st.p[q][1]) + (st.p[q][2] + st.p[q][3]);
+        for (int q = 0; q < NQ; ++q) st.x[q] = st.p[q];
       } else if (k == NE + 1) {
-        // sum of both swap outputs: the pair's total in every lane, whichever way it swaps
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(st.x[q]), __float_as_uint(st.x[q]), false, false);
-          st.x[q] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+        if constexpr (NQ == 2) {
+          // one swap for both queries: row 2m + 1 of query 0 trades places with row 2m of query
+          // 1, so the sum of the outputs holds in row r the pair sum of query r % 2
+          const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(st.x[0]), __float_as_uint(st.x[1]), false, false);
+          st.x[0] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+        } else {
+          // sum of both swap outputs: the pair's total in every lane, whichever way it swaps
+          const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(st.x[0]), __float_as_uint(st.x[0]), false, false);
+          st.x[0] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
         }
       } else if (k == NE + 2) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.x[q]), __float_as_uint(st.x[q]), false, false);
-          st.x[q] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
-        }
+        // rows r and r + 2 meet: every row holds its query's total
+        const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.x[0]), __float_as_uint(st.x[0]), false, false);
+        st.x[0] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
       } else {
         // branch-free (a branch would end the interleave): masked lanes write to their own sink
-        // words; a block before the first (i = -1) has a negative offset
-        const float v = ((NQ == 2 && g == 1) ? st.x[NQ - 1] : st.x[0]) * sc;
+        // words; a block before the first (i = -1) has a negative offset. Row g holds the total
+        // of query g % 2 (the only one with one query)
+        const float v = st.x[0] * sc;
         const int jl = (i * NW + wave) * DC_KB + n;             // offset in the sub-chunk
         const bool valid = owner & ((unsigned)jl < (unsigned)(sub1 - sub0));
         *(valid ? my_ssc + jl : sink_f) = v;
@@ -335,7 +339,7 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
           } else {
             issue_keys_at(key_of(i + PF), raw[u]);
           }
-          float p[NQ][4];
+          float p[NQ];
           f32x4v_t ac[2][NQ];
           auto mm = [&](int hb, f32x4v_t (&o)[NQ]) {
 #pragma unroll
@@ -350,7 +354,7 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
 #pragma unroll
               for (int q = 0; q < NQ; ++q) {
                 const float t = __int_as_float(max(__float_as_int(o[q][r]), 0));
-                p[q][r] = hb == 0 ? wv[q][hb][r] * t : fmaf(wv[q][hb][r], t, p[q][r]);
+                p[q] = hb == 0 && r == 0 ? wv[q][hb][r] * t : fmaf(wv[q][hb][r], t, p[q]);
               }
           };
           mm(0, ac[0]);
@@ -362,9 +366,7 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
           ep(HB - 1, ac[(HB - 1) & 1]);
           Epi st;
 #pragma unroll
-          for (int q = 0; q < NQ; ++q)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st.p[q][r] = p[q][r];
+          for (int q = 0; q < NQ; ++q) st.p[q] = p[q];
 #pragma unroll
           for (int k = NE; k < NPIECE; ++k) piece(k, st, i, acc[0], scl[u]);   // (no accumulator read)
           // the slot's scale is used: refill it with block i + PF's
@@ -1071,7 +1073,7 @@ size_t decode_scan_lds(int keep) {
 
 template <int D, int HB, int KST>
 static hipError_t launch_scan(const DecodeArgs& a, hipStream_t s) {
-  constexpr int W = DC_SCAN_WAVES, PF = dc_pf<KST, W>();
+  constexpr int W = D == 64 ? 8 : 4, PF = dc_pf<KST, W>();
   const bool blk = a.blocks != nullptr;
   // one query per work-group (pairs of one, or a single query per sequence): half the MFMAs and
   // epilogue per key block
