@@ -415,28 +415,30 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // ---- the sub-chunk's scores of row qq as order-preserving keys in registers, half a row at a
-    // time: thread tid takes slots j = 1024 st + 4 tid + e (0, below every score's key, past the
-    // row's visible slots; loads past them stay inside the score area)
-    constexpr int MST = DC_SUB / (4 * NT), HST = MST / 2;
+    // ---- the sub-chunk's scores of row qq as order-preserving keys in registers, CST steps of
+    // 4 NT slots at a time (the nck chunks that hold the sub-chunk): thread tid takes slots
+    // j = 4 NT st + 4 tid + e (0, below every score's key, past the row's visible slots; loads
+    // past them stay inside the score area)
+    constexpr int CST = 4;
     const int len = sub1 - sub0;
-    auto load_keys = [&](int qq, int h, uint32_t (&kr)[HST][4]) {
+    const int nck = (len + CST * 4 * NT - 1) / (CST * 4 * NT);
+    auto load_keys = [&](int qq, int h, uint32_t (&kr)[CST][4]) {
       int lim = min(len, (qq ? V1 : V0) - sub0);                   // visible slots
       asm volatile("" : "+s"(lim));       // the masks are recomputed per call, not kept (64 pairs)
       const float* row = ssc + qq * a.sub + 4 * tid;
-      f32x4_t v[HST];
+      f32x4_t v[CST];
 #pragma unroll
-      for (int u = 0; u < HST; ++u) v[u] = *reinterpret_cast<const f32x4_t*>(row + (h * HST + u) * 4 * NT);
+      for (int u = 0; u < CST; ++u) v[u] = *reinterpret_cast<const f32x4_t*>(row + (h * CST + u) * 4 * NT);
       __builtin_amdgcn_sched_barrier(0);         // the loads in flight together
-      if (lim >= MST * 4 * NT) {                           // every slot visible
+      if (lim >= (h + 1) * CST * 4 * NT) {                         // every slot visible
 #pragma unroll
-        for (int u = 0; u < HST; ++u)
+        for (int u = 0; u < CST; ++u)
 #pragma unroll
           for (int e = 0; e < 4; ++e) kr[u][e] = f2key3(v[u][e]);
       } else {
 #pragma unroll
-        for (int u = 0; u < HST; ++u) {
-          const int j = (h * HST + u) * 4 * NT + 4 * tid;
+        for (int u = 0; u < CST; ++u) {
+          const int j = (h * CST + u) * 4 * NT + 4 * tid;
 #pragma unroll
           for (int e = 0; e < 4; ++e) kr[u][e] = j + e < lim ? f2key3(v[u][e]) : 0u;
           __builtin_amdgcn_sched_barrier(0);     // a few compare masks live at a time, not 32
@@ -450,12 +452,11 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
       if (qq < nrows) {
         uint32_t* hq = hist + qq * 2048;
         uint32_t* hsink = sink + 64 + lane;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t kr[HST][4];
+        for (int h = 0; h < nck; ++h) {
+          uint32_t kr[CST][4];
           load_keys(qq, h, kr);
 #pragma unroll
-          for (int u = 0; u < HST; ++u) {
+          for (int u = 0; u < CST; ++u) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               // branch-free: a hidden or -inf slot adds to the lane's own sink word
@@ -544,12 +545,11 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
         // a candidate: a finite score's key at or above the bound (keys of hidden slots are 0)
         const uint32_t thr = max(misc[4 * qq], KEY_NEG_INF + 1u);
         uint32_t n = 0;                                              // the wave's count
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t kr[HST][4];
+        for (int h = 0; h < nck; ++h) {
+          uint32_t kr[CST][4];
           load_keys(qq, h, kr);
 #pragma unroll
-          for (int u = 0; u < HST; ++u) {
+          for (int u = 0; u < CST; ++u) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) n += (uint32_t)__popcll(__ballot(kr[u][e] >= thr));
             __builtin_amdgcn_sched_barrier(0);
@@ -563,12 +563,11 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
         uint8_t* ck = reinterpret_cast<uint8_t*>(a.cand_key + rr * a.cand_cap);
         uint8_t* ci = reinterpret_cast<uint8_t*>(a.cand_idx + rr * a.cand_cap);
         const uint32_t slot0 = (uint32_t)(sub0 + 4 * tid);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t kr[HST][4];
+        for (int h = 0; h < nck; ++h) {
+          uint32_t kr[CST][4];
           load_keys(qq, h, kr);
 #pragma unroll
-          for (int u = 0; u < HST; ++u) {
+          for (int u = 0; u < CST; ++u) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t x = kr[u][e];
@@ -577,7 +576,7 @@ __global__ void __launch_bounds__(W * 64, 1) decode_scan_kernel(DecodeArgs a) {
               if (f) {
                 const uint32_t at = 4u * (pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)));
                 *reinterpret_cast<uint32_t*>(ck + at) = x;
-                *reinterpret_cast<uint32_t*>(ci + at) = slot0 + (uint32_t)((h * HST + u) * 4 * NT + e);
+                *reinterpret_cast<uint32_t*>(ci + at) = slot0 + (uint32_t)((h * CST + u) * 4 * NT + e);
               }
               pos += (uint32_t)__popcll(m);
               __builtin_amdgcn_sched_barrier(0);                   // one register's masks live at a time
