@@ -825,9 +825,13 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
         }
       }
     }
-    // selected: above b1 (every candidate when all are taken); bin-b1 candidates: in b1
-    auto is_sel = [&](uint32_t x, uint32_t bb) { return (x > KEY_NEG_INF) & (all | ((x >> 20) > bb)); };
-    auto is_cand = [&](uint32_t x, uint32_t bb) { return (x > KEY_NEG_INF) & !all & ((x >> 20) == bb); };
+    // selected: above b1 (every candidate when all are taken); bin-b1 candidates: in b1. One
+    // compare each on the key (candidates are finite, so b1 >= 8 unless all are taken; an empty
+    // register holds 0, neither)
+    const uint32_t sel_gt = all ? KEY_NEG_INF : (uint32_t)(((uint64_t)b1 + 1u << 20) - 1u);
+    const uint32_t clo = b1 << 20, cwid = all ? 0u : (1u << 20);
+    auto is_sel = [&](uint32_t x, uint32_t) { return x > sel_gt; };
+    auto is_cand = [&](uint32_t x, uint32_t) { return x - clo < cwid; };
     // per-wave counts, then each wave writes its candidates from its own offsets
     uint32_t cs = 0, cq = 0;                               // this lane's counts
 #pragma unroll
@@ -869,25 +873,34 @@ __global__ void __launch_bounds__(RS_THREADS) decode_select_kernel(DecodeArgs a)
     if (stage) {
       // lane order instead of chunk order: each lane writes its own entries from its offset (the
       // exclusive scan of the counts above), without ballots, without branches (an entry a lane
-      // does not keep goes to its own sink words)
+      // does not keep goes to its own sink words); chunks in groups of 4 (one uniform test each)
       uint32_t ls = ps + cs - cs_own, lc = pc + cq - cq_own;
+      auto emit = [&](auto spill_tag) {
+        constexpr bool SPILL = decltype(spill_tag)::value;       // bin-b1 candidates past the LDS
 #pragma unroll
-      for (int u = 0; u < RS_R; ++u) {
-        if (u >= nchk) continue;
-        const bool sel = is_sel(xr[u], b1x), cand = is_cand(xr[u], b1x);
-        const uint32_t at = (sel && ls < (uint32_t)(DC_BINS / 2)) ? 2u * ls : (uint32_t)DC_BINS + 2u * (uint32_t)lane;
-        hist[at] = ir[u];
-        hist[at + 1] = xr[u];
-        const uint32_t cl = (cand && lc < (uint32_t)RS_LDS_CAND) ? lc : (uint32_t)RS_LDS_CAND + (uint32_t)lane;
-        ckey[cl] = xr[u];
-        cpos[cl] = ir[u];
-        if (cand && lc >= (uint32_t)RS_LDS_CAND) {
-          g2k[lc] = xr[u];
-          g2p[lc] = ir[u];
+        for (int u0 = 0; u0 < RS_R; u0 += 4) {
+          if (u0 >= nchk) break;
+#pragma unroll
+          for (int u = u0; u < u0 + 4; ++u) {
+            const bool sel = is_sel(xr[u], b1x), cand = is_cand(xr[u], b1x);
+            // (fewer than kk <= DC_BINS / 2 are selected here, so ls stays inside the staging area)
+            const uint32_t at = sel ? 2u * ls : (uint32_t)DC_BINS + 2u * (uint32_t)lane;
+            hist[at] = ir[u];
+            hist[at + 1] = xr[u];
+            const uint32_t cl = (cand && (!SPILL || lc < (uint32_t)RS_LDS_CAND)) ? lc : (uint32_t)RS_LDS_CAND + (uint32_t)lane;
+            ckey[cl] = xr[u];
+            cpos[cl] = ir[u];
+            if (SPILL && cand && lc >= (uint32_t)RS_LDS_CAND) {
+              g2k[lc] = xr[u];
+              g2p[lc] = ir[u];
+            }
+            ls += sel ? 1u : 0u;
+            lc += cand ? 1u : 0u;
+          }
         }
-        ls += sel ? 1u : 0u;
-        lc += cand ? 1u : 0u;
-      }
+      };
+      if (pc + (uint32_t)__builtin_amdgcn_readfirstlane(wsum[RS_WAVES + wave]) <= (uint32_t)RS_LDS_CAND) emit(std::false_type{});
+      else emit(std::true_type{});
     }
 #pragma unroll
     for (int u = 0; u < RS_R; ++u) {
