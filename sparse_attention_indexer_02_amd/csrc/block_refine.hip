@@ -181,21 +181,25 @@ block_refine_kernel(BlockRefineArgs a) {
 }
 
 // bf16 keys and queries: the union's key rows stream straight into LDS (global_load_lds, 128-key
-// tiles, double-buffered) and a wave that owns all four 32-key steps of a tile runs them
+// tiles in a ring of NBUF buffers, loads issued NBUF - 1 tiles ahead: the union's blocks are
+// scattered over the cache, so a tile's rows come from L2, the MALL or HBM with a latency longer
+// than one tile's MFMA work) and a wave that owns all four 32-key steps of a tile runs them
 // pipelined (the epilogue of one step under the MFMAs of the next, the next step's fragments read
 // during the current step), as the dense score kernel does; partly owned tiles run step by step.
-template <int D, int HB>
+template <int D, int HB, int NBUF, bool BIG>
 __global__ void __launch_bounds__(WavesFor<HB>::value * 64)
 block_refine_direct_kernel(BlockRefineArgs a) {
   constexpr int NW = WavesFor<HB>::value;
   constexpr int NTHR = NW * 64;
   constexpr int KT = 128;
   constexpr int NSUB = KT / 32;
+  constexpr int DIST = NBUF - 1;                    // tiles in flight ahead of the one in use
+  static_assert(NBUF == 2 || NBUF == 3, "ring of two or three tiles");
   typedef Geo<MmaBf16, D, KT> G;
   typedef DirectLoader<MmaBf16, D, NTHR, KT> DLoader;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tiles = smem;
-  int16_t* pos_tab = reinterpret_cast<int16_t*>(smem + 2 * G::TILE_BYTES);   // [NW][UMAX]
+  int16_t* pos_tab = reinterpret_cast<int16_t*>(smem + NBUF * G::TILE_BYTES);   // [NW][UMAX]
   int32_t* ublk = reinterpret_cast<int32_t*>(pos_tab + NW * BR_UMAX);        // [UMAX]
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(ublk + BR_UMAX);            // [NBW]
   uint32_t* wpre = bitmap + BR_NBW;                                          // [NBW]
@@ -306,30 +310,130 @@ block_refine_direct_kernel(BlockRefineArgs a) {
     __syncthreads();
 
     const int nslots = rcount * Bs;
+    const int ntile = (nslots + KT - 1) / KT;
+    bf16x8_t bfr[G::NKK];
+    // the four steps of a tile the wave's query owns entirely, pipelined; scores two steps per
+    // value: lanes 0-31 hold the even step, lanes 32-63 the odd one
+    auto full_tile = [&](const uint8_t* tile, float (&ov)[NSUB / 2]) {
+      auto put = [&](int st, float tot) {
+        if ((st & 1) == (lane >> 5)) ov[st >> 1] = tot;
+      };
+      f32x16_t A[HB], Bq[HB];
+      load_bfrag<MmaBf16, D, KT>(tile, 0, lane, bfr);
+      tile_mma_rot<D, HB, KT>(qf, bfr, tile, 32, true, lane, A);
+#pragma unroll
+      for (int s = 1; s < NSUB; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (s & 1) {
+          tile_mma_rot<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, lane, Bq);
+          put(s - 1, tile_epilogue<HB>(A, wv));
+        } else {
+          tile_mma_rot<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, lane, A);
+          put(s - 1, tile_epilogue<HB>(Bq, wv));
+        }
+#pragma unroll
+        for (int kk = 0; kk < G::NKK; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(0x008, HB, 0);
+          if (s + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (16 * HB * 2 + 8) / G::NKK + 1, 0);
+        }
+      }
+      put(NSUB - 1, tile_epilogue<HB>(Bq, wv));
+    };
+    // Ring discipline: tile j lives in buffer j % NBUF; the loads of tile it + DIST are issued at
+    // the start of iteration it, into the buffer that every wave finished reading in iteration
+    // it - 1 (the barrier ending that iteration). Loads return in issue order, so "at most
+    // ITERS outstanding" once the next tile's loads are issued means tile it + 1 has landed.
+    if constexpr (BIG) {
+      // Blocks of KT keys or more: a tile is KT consecutive keys of one union block, so all it
+      // takes is the tile's first key and the block's kept position for this wave's query (-1:
+      // not kept). Lane j holds both for tile w0 + j of a 64-tile window, read from LDS once per
+      // window; a tile's values are then taken with readlane, with no LDS round trip in the tile
+      // loop. Every tile is full (the union's slot count is a multiple of Bs).
+      int k0_win = 0, m_win = -1, w0 = 0;
+      auto refresh = [&](int first) {
+        const int j = first + lane;
+        const int v = j * KT;
+        k0_win = j < ntile ? (ublk[v >> lb] << lb) + (v & (Bs - 1)) : 0;
+        m_win = (active && j < ntile) ? (int)pos_tab[wave * BR_UMAX + (v >> lb)] : -1;
+      };
+      auto load_tile = [&](int j, int k0) {
+        int kx[DLoader::ITERS];
+#pragma unroll
+        for (int i = 0; i < DLoader::ITERS; ++i) {
+          const int key = k0 + DLoader::row_of(i, wave, lane);
+          kx[i] = key < kl ? key : -1;
+        }
+        DLoader::load_idx(kseq, tiles + (j % NBUF) * G::TILE_BYTES, wave, lane, kx);
+      };
+      refresh(0);
+#pragma unroll
+      for (int j = 0; j < DIST; ++j)
+        if (j < ntile) load_tile(j, __builtin_amdgcn_readlane(k0_win, j));
+      if (DIST == 2 && ntile > 1) wait_vmem_n<DLoader::ITERS>();
+      else wait_vmem();
+      lds_barrier();
+      for (int it = 0; it < ntile; ++it) {
+        const bool more = it + 1 < ntile;
+        if (it + DIST >= w0 + 64) {                     // the window covers tiles it .. it + DIST
+          w0 = it;
+          refresh(w0);
+        }
+        if (it + DIST < ntile) load_tile(it + DIST, __builtin_amdgcn_readlane(k0_win, it + DIST - w0));
+        const int k0_cur = __builtin_amdgcn_readlane(k0_win, it - w0);
+        const int m_cur = __builtin_amdgcn_readlane(m_win, it - w0);
+        float ov[NSUB / 2];
+        if (m_cur >= 0) full_tile(tiles + (it % NBUF) * G::TILE_BYTES, ov);
+        if (DIST == 2 && it + 2 < ntile) wait_vmem_n<DLoader::ITERS>();
+        else if (more) wait_vmem();
+        if (m_cur >= 0) {
+          const int sbase = (m_cur << lb) + ((it * KT) & (Bs - 1));
+#pragma unroll
+          for (int p = 0; p < NSUB / 2; ++p) {
+            const int o = (2 * p + (lane >> 5)) * 32 + (lane & 31);
+            const int key = k0_cur + o;
+            srow[sbase + o] = (key < kl && key <= my_pos) ? ov[p] : -INFINITY;
+          }
+        }
+        lds_barrier();
+      }
+      continue;
+    }
     auto key_at = [&](int v) -> int {                // key of union slot v, or -1
       if (v >= nslots) return -1;
       const int key = (ublk[v >> lb] << lb) + (v & (Bs - 1));
       return key < kl ? key : -1;
     };
-    const int ntile = (nslots + KT - 1) / KT;
     int kidx[DLoader::ITERS];
     auto fetch_idx = [&](int base) {
 #pragma unroll
       for (int i = 0; i < DLoader::ITERS; ++i) kidx[i] = key_at(base + DLoader::row_of(i, wave, lane));
     };
-    fetch_idx(0);
-    DLoader::load_idx(kseq, tiles, wave, lane, kidx);
-    if (ntile > 1) fetch_idx(KT);
-    wait_vmem();
-    __syncthreads();
-    bf16x8_t bfr[G::NKK];
+    {
+      // every index is read from LDS before the first load goes out (an LDS read after the
+      // loads would wait for them)
+      int kj[DIST][DLoader::ITERS];
+#pragma unroll
+      for (int j = 0; j < DIST; ++j) {
+        fetch_idx(j * KT);
+#pragma unroll
+        for (int i = 0; i < DLoader::ITERS; ++i) kj[j][i] = kidx[i];
+      }
+      fetch_idx(DIST * KT);
+#pragma unroll
+      for (int j = 0; j < DIST; ++j)
+        if (j < ntile) DLoader::load_idx(kseq, tiles + j * G::TILE_BYTES, wave, lane, kj[j]);
+    }
+    if (DIST == 2 && ntile > 1) wait_vmem_n<DLoader::ITERS>();
+    else wait_vmem();
+    lds_barrier();
     for (int it = 0; it < ntile; ++it) {
-      const int cur = it & 1;
+      const int cur = it % NBUF;
       const int base = it * KT;
       const bool more = it + 1 < ntile;
-      if (more) {
-        DLoader::load_idx(kseq, tiles + (cur ^ 1) * G::TILE_BYTES, wave, lane, kidx);
-        if (it + 2 < ntile) fetch_idx(base + 2 * KT);
+      if (it + DIST < ntile) {
+        DLoader::load_idx(kseq, tiles + ((it + DIST) % NBUF) * G::TILE_BYTES, wave, lane, kidx);
+        if (it + DIST + 1 < ntile) fetch_idx(base + (DIST + 1) * KT);
       }
       const uint8_t* tile = tiles + cur * G::TILE_BYTES;
       // kept position of a union slot's block for this wave's query, or -1
@@ -340,35 +444,11 @@ block_refine_direct_kernel(BlockRefineArgs a) {
       for (int s = 0; s < NSUB; ++s)
         if (__ballot(kept_pos(base + s * 32 + (lane & 31)) >= 0) != 0ull) own |= 1u << s;
       if (!active) own = 0;
-      // scores, two steps per value: lanes 0-31 hold the even step, lanes 32-63 the odd one
       float ov[NSUB / 2];
 #pragma unroll
       for (int p = 0; p < NSUB / 2; ++p) ov[p] = 0.f;
-      auto put = [&](int st, float tot) {
-        if ((st & 1) == (lane >> 5)) ov[st >> 1] = tot;
-      };
       if (own == (1u << NSUB) - 1u) {
-        f32x16_t A[HB], Bq[HB];
-        load_bfrag<MmaBf16, D, KT>(tile, 0, lane, bfr);
-        tile_mma_rot<D, HB, KT>(qf, bfr, tile, 32, true, lane, A);
-#pragma unroll
-        for (int s = 1; s < NSUB; ++s) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (s & 1) {
-            tile_mma_rot<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, lane, Bq);
-            put(s - 1, tile_epilogue<HB>(A, wv));
-          } else {
-            tile_mma_rot<D, HB, KT>(qf, bfr, tile, (s + 1) * 32, s + 1 < NSUB, lane, A);
-            put(s - 1, tile_epilogue<HB>(Bq, wv));
-          }
-#pragma unroll
-          for (int kk = 0; kk < G::NKK; ++kk) {
-            __builtin_amdgcn_sched_group_barrier(0x008, HB, 0);
-            if (s + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, (16 * HB * 2 + 8) / G::NKK + 1, 0);
-          }
-        }
-        put(NSUB - 1, tile_epilogue<HB>(Bq, wv));
+        full_tile(tile, ov);
       } else {
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
@@ -376,11 +456,14 @@ block_refine_direct_kernel(BlockRefineArgs a) {
             f32x16_t acc[HB];
             load_bfrag<MmaBf16, D, KT>(tile, s * 32, lane, bfr);
             tile_mma_rot<D, HB, KT>(qf, bfr, tile, 0, false, lane, acc);
-            put(s, tile_epilogue<HB>(acc, wv));
+            const float tot = tile_epilogue<HB>(acc, wv);
+            if ((s & 1) == (lane >> 5)) ov[s >> 1] = tot;
           }
         }
       }
-      if (more) wait_vmem();
+      // tile it + 1 landed (this wave's share; the barrier below covers the others')
+      if (DIST == 2 && it + 2 < ntile) wait_vmem_n<DLoader::ITERS>();
+      else if (more) wait_vmem();
       // lanes 0-31 store the even steps, lanes 32-63 the odd ones
 #pragma unroll
       for (int p = 0; p < NSUB / 2; ++p) {
@@ -427,13 +510,15 @@ static hipError_t launch_br_dh(const BlockRefineArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int D, int HB>
+template <int D, int HB, int NBUF, bool BIG>
 static hipError_t launch_brd(const BlockRefineArgs& a, hipStream_t s) {
   constexpr int NW = WavesFor<HB>::value;
   typedef Geo<MmaBf16, D, 128> G;
-  const size_t lds = 2 * G::TILE_BYTES + NW * BR_UMAX * sizeof(int16_t) +
+  const size_t lds = NBUF * G::TILE_BYTES + NW * BR_UMAX * sizeof(int16_t) +
                      BR_UMAX * sizeof(int32_t) + 2 * BR_NBW * sizeof(uint32_t) + 80 * sizeof(uint32_t);
-  auto kfn = block_refine_direct_kernel<D, HB>;
+  static_assert(NBUF * G::TILE_BYTES + NW * BR_UMAX * 2 + BR_UMAX * 4 + 2 * BR_NBW * 4 + 320 <= 160 * 1024,
+                "LDS of one work-group");
+  auto kfn = block_refine_direct_kernel<D, HB, NBUF, BIG>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -445,8 +530,11 @@ hipError_t launch_block_refine(const BlockRefineArgs& a, hipStream_t s) {
   if (a.q_dtype == DT_BF16 && a.k_dtype == DT_BF16) {
     const int HB = (a.H + 31) / 32;
     const bool pow2 = (a.block_size & (a.block_size - 1)) == 0;
-    if (pow2 && a.D == 128 && HB <= 2) return launch_brd<128, 2>(a, s);
-    if (pow2 && a.D == 64 && HB <= 2) return launch_brd<64, 2>(a, s);
+    const bool big = a.block_size >= 128;       // blocks of at least one 128-key tile
+    if (pow2 && a.D == 128 && HB <= 2)
+      return big ? launch_brd<128, 2, 3, true>(a, s) : launch_brd<128, 2, 3, false>(a, s);
+    if (pow2 && a.D == 64 && HB <= 2)
+      return big ? launch_brd<64, 2, 3, true>(a, s) : launch_brd<64, 2, 3, false>(a, s);
     return launch_br_dh<MmaBf16, DT_BF16>(a, s);
   }
   if (a.k_dtype == DT_F32) return launch_br_dh<MmaF32, DT_F32>(a, s);

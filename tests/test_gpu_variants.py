@@ -147,6 +147,16 @@ def test_block_sizes(Bs, keep):
                 f"block-Bs{Bs}")
 
 
+@pytest.mark.parametrize("Bs,keep", [(128, 40), (256, 20), (512, 8)])
+def test_block_whole_tile_blocks(Bs, keep):
+    # blocks of one or more 128-key tiles at H=64, D=128 (the path that takes a tile's keys and
+    # kept position per tile), a partial last block, unions of more than 64 tiles
+    p = W.make_hier(13000, 96, seed=40 + Bs, n_regions=6, region=Bs)
+    say(f"case block Bs={Bs} keep={keep} N=13000 T=96 H=64 D=128")
+    gi, gs, gb = run_block(p, 256, Bs, keep)
+    check_block(p, 256, Bs, keep, gi, gs, gb, [(0, t) for t in range(p.T)], f"block-big-Bs{Bs}")
+
+
 def test_block_keep_all_is_dense():
     p = W.make_hier(1500, 100, H=32, D=128, seed=34)
     say("case block keep >= blocks (must equal dense)")
