@@ -13,6 +13,13 @@
 
 namespace idx {
 
+// Waits until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 constexpr int BR_UMAX = 2048;        // union blocks handled per round
 constexpr int BR_NBW = 2048;         // bitmap words: blocks per sequence <= 65536
 

@@ -160,12 +160,6 @@ struct DirectLoader {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Waits until at most N of this wave's vector memory operations are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Work-group barrier for reusing LDS tiles: waits for this wave's LDS operations only, then
 // s_barrier. Unlike __syncthreads() it does not first wait for the wave's global stores (the
