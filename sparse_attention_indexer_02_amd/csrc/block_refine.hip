@@ -22,6 +22,7 @@ __device__ __forceinline__ void wait_vmem_n() {
 
 constexpr int BR_UMAX = 2048;        // union blocks handled per round
 constexpr int BR_NBW = 2048;         // bitmap words: blocks per sequence <= 65536
+constexpr int BRD_UMAX = 1024;       // union blocks per round of the direct kernel
 
 template <class Mma, int D, int HB, int KST>
 __global__ void __launch_bounds__(WavesFor<HB>::value * 64)
@@ -193,10 +194,9 @@ block_refine_kernel(BlockRefineArgs a) {
 // than one tile's MFMA work) and a wave that owns all four 32-key steps of a tile runs them
 // pipelined (the epilogue of one step under the MFMAs of the next, the next step's fragments read
 // during the current step), as the dense score kernel does; partly owned tiles run step by step.
-template <int D, int HB, int NBUF, bool BIG>
-__global__ void __launch_bounds__(WavesFor<HB>::value * 64)
+template <int D, int HB, int NBUF, bool BIG, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 block_refine_direct_kernel(BlockRefineArgs a) {
-  constexpr int NW = WavesFor<HB>::value;
   constexpr int NTHR = NW * 64;
   constexpr int KT = 128;
   constexpr int NSUB = KT / 32;
@@ -206,11 +206,13 @@ block_refine_direct_kernel(BlockRefineArgs a) {
   typedef DirectLoader<MmaBf16, D, NTHR, KT> DLoader;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tiles = smem;
-  int16_t* pos_tab = reinterpret_cast<int16_t*>(smem + NBUF * G::TILE_BYTES);   // [NW][UMAX]
-  int32_t* ublk = reinterpret_cast<int32_t*>(pos_tab + NW * BR_UMAX);        // [UMAX]
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(ublk + BR_UMAX);            // [NBW]
-  uint32_t* wpre = bitmap + BR_NBW;                                          // [NBW]
-  uint32_t* sh = wpre + BR_NBW;                                              // [80]
+  // the bitmap holds the sequence's blocks: (ceil(N / Bs) + 31) / 32 words, sized at launch
+  const int nbw_cap = ((a.N + a.block_size - 1) / a.block_size + 31) / 32;
+  int16_t* pos_tab = reinterpret_cast<int16_t*>(smem + NBUF * G::TILE_BYTES);   // [NW][BRD_UMAX]
+  int32_t* ublk = reinterpret_cast<int32_t*>(pos_tab + NW * BRD_UMAX);       // [BRD_UMAX]
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(ublk + BRD_UMAX);           // [nbw_cap]
+  uint32_t* wpre = bitmap + nbw_cap;                                         // [nbw_cap]
+  uint32_t* sh = wpre + nbw_cap;                                             // [80]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -289,8 +291,8 @@ block_refine_direct_kernel(BlockRefineArgs a) {
   const uint8_t* kseq = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)b * a.N * (D * 2);
   float* srow = a.scores + ((int64_t)b * a.rows_per_seq + (active ? t - a.t0 : 0)) * a.score_stride;
 
-  for (uint32_t rb = 0; rb < n_union; rb += BR_UMAX) {
-    const int rcount = (int)min((uint32_t)BR_UMAX, n_union - rb);
+  for (uint32_t rb = 0; rb < n_union; rb += BRD_UMAX) {
+    const int rcount = (int)min((uint32_t)BRD_UMAX, n_union - rb);
     {
       const int per = (NBW + NTHR - 1) / NTHR;
       const int w0 = tid * per;
@@ -306,13 +308,13 @@ block_refine_direct_kernel(BlockRefineArgs a) {
           ++u;
         }
       }
-      for (int i = tid; i < NW * rcount; i += NTHR) pos_tab[(i / rcount) * BR_UMAX + i % rcount] = -1;
+      for (int i = tid; i < NW * rcount; i += NTHR) pos_tab[(i / rcount) * BRD_UMAX + i % rcount] = -1;
     }
     __syncthreads();
     for (int p = lane; p < nk; p += 64) {
       const int blk = mylist[p];
       const uint32_t u = wpre[blk >> 5] + __popc(bitmap[blk >> 5] & ((1u << (blk & 31)) - 1u));
-      if (u >= rb && u < rb + (uint32_t)rcount) pos_tab[wave * BR_UMAX + (u - rb)] = (int16_t)p;
+      if (u >= rb && u < rb + (uint32_t)rcount) pos_tab[wave * BRD_UMAX + (u - rb)] = (int16_t)p;
     }
     __syncthreads();
 
@@ -362,7 +364,7 @@ block_refine_direct_kernel(BlockRefineArgs a) {
         const int j = first + lane;
         const int v = j * KT;
         k0_win = j < ntile ? (ublk[v >> lb] << lb) + (v & (Bs - 1)) : 0;
-        m_win = (active && j < ntile) ? (int)pos_tab[wave * BR_UMAX + (v >> lb)] : -1;
+        m_win = (active && j < ntile) ? (int)pos_tab[wave * BRD_UMAX + (v >> lb)] : -1;
       };
       auto load_tile = [&](int j, int k0) {
         int kx[DLoader::ITERS];
@@ -444,7 +446,7 @@ block_refine_direct_kernel(BlockRefineArgs a) {
       }
       const uint8_t* tile = tiles + cur * G::TILE_BYTES;
       // kept position of a union slot's block for this wave's query, or -1
-      auto kept_pos = [&](int v) -> int { return v < nslots ? pos_tab[wave * BR_UMAX + (v >> lb)] : -1; };
+      auto kept_pos = [&](int v) -> int { return v < nslots ? pos_tab[wave * BRD_UMAX + (v >> lb)] : -1; };
       // steps holding at least one of the query's blocks (lanes l and l + 32 share key l % 32)
       uint32_t own = 0;
 #pragma unroll
@@ -517,15 +519,17 @@ static hipError_t launch_br_dh(const BlockRefineArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int D, int HB, int NBUF, bool BIG>
-static hipError_t launch_brd(const BlockRefineArgs& a, hipStream_t s) {
-  constexpr int NW = WavesFor<HB>::value;
+template <int D, int HB, int NBUF, bool BIG, int NW>
+static hipError_t launch_brd(const BlockRefineArgs& a0, hipStream_t s) {
   typedef Geo<MmaBf16, D, 128> G;
-  const size_t lds = NBUF * G::TILE_BYTES + NW * BR_UMAX * sizeof(int16_t) +
-                     BR_UMAX * sizeof(int32_t) + 2 * BR_NBW * sizeof(uint32_t) + 80 * sizeof(uint32_t);
-  static_assert(NBUF * G::TILE_BYTES + NW * BR_UMAX * 2 + BR_UMAX * 4 + 2 * BR_NBW * 4 + 320 <= 160 * 1024,
-                "LDS of one work-group");
-  auto kfn = block_refine_direct_kernel<D, HB, NBUF, BIG>;
+  BlockRefineArgs a = a0;
+  a.tiles_per_seq = (a.t1 - a.t0 + NW - 1) / NW;             // NW queries per work-group
+  const size_t nbw_cap = ((size_t)(a.N + a.block_size - 1) / a.block_size + 31) / 32;
+  const size_t lds = NBUF * G::TILE_BYTES + NW * BRD_UMAX * sizeof(int16_t) +
+                     BRD_UMAX * sizeof(int32_t) + 2 * nbw_cap * sizeof(uint32_t) + 80 * sizeof(uint32_t);
+  static_assert(NBUF * G::TILE_BYTES + NW * BRD_UMAX * 2 + BRD_UMAX * 4 + 2 * BR_NBW * 4 + 320 <= 160 * 1024,
+                "LDS of one work-group at the largest bitmap");
+  auto kfn = block_refine_direct_kernel<D, HB, NBUF, BIG, NW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -539,9 +543,9 @@ hipError_t launch_block_refine(const BlockRefineArgs& a, hipStream_t s) {
     const bool pow2 = (a.block_size & (a.block_size - 1)) == 0;
     const bool big = a.block_size >= 128;       // blocks of at least one 128-key tile
     if (pow2 && a.D == 128 && HB <= 2)
-      return big ? launch_brd<128, 2, 3, true>(a, s) : launch_brd<128, 2, 3, false>(a, s);
+      return big ? launch_brd<128, 2, 2, true, 4>(a, s) : launch_brd<128, 2, 2, false, 4>(a, s);
     if (pow2 && a.D == 64 && HB <= 2)
-      return big ? launch_brd<64, 2, 3, true>(a, s) : launch_brd<64, 2, 3, false>(a, s);
+      return big ? launch_brd<64, 2, 2, true, 4>(a, s) : launch_brd<64, 2, 2, false, 4>(a, s);
     return launch_br_dh<MmaBf16, DT_BF16>(a, s);
   }
   if (a.k_dtype == DT_F32) return launch_br_dh<MmaF32, DT_F32>(a, s);
