@@ -157,6 +157,16 @@ def test_block_whole_tile_blocks(Bs, keep):
     check_block(p, 256, Bs, keep, gi, gs, gb, [(0, t) for t in range(p.T)], f"block-big-Bs{Bs}")
 
 
+@pytest.mark.parametrize("N,T,Bs,keep", [(40000, 32, 16, 900), (200000, 16, 128, 500)])
+def test_block_union_of_several_rounds(N, T, Bs, keep):
+    # uncorrelated queries: the union of a work-group's kept blocks exceeds the 1024 blocks the
+    # refine handles per round (counted on the CPU: ~1100 blocks at Bs=128), so it runs in rounds
+    p = W.make_hier(N, T, seed=50 + Bs, rho=0.0)
+    say(f"case block rounds N={N} T={T} Bs={Bs} keep={keep} H=64 D=128")
+    gi, gs, gb = run_block(p, 512, Bs, keep)
+    check_block(p, 512, Bs, keep, gi, gs, gb, [(0, t) for t in range(p.T)], f"block-rounds-Bs{Bs}")
+
+
 def test_block_keep_all_is_dense():
     p = W.make_hier(1500, 100, H=32, D=128, seed=34)
     say("case block keep >= blocks (must equal dense)")
