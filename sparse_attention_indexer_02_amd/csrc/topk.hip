@@ -246,7 +246,11 @@ __global__ void __launch_bounds__(TK_THREADS) topk_long_kernel(TopkArgs a) {
 // (16-byte loads, all issued before use). Digit histograms (11/11/10 bits) are built with LDS
 // atomics from the registers; each threshold search runs in a single wave with DPP scans; the
 // ordered output takes per-lane counts, one DPP scan per 256-slot block and one table of wave
-// totals.
+// totals. A row's scores span a narrow range (one query's scores: a few binary exponents), so
+// the keys are first re-based on the row: v = (x - min) << s + 2^23 (s aligns the row's range
+// to bit 30) maps the finite keys one to one and in order onto the upper part of the key space,
+// which spreads them over ~1024 first-digit bins instead of a handful, where the histogram's
+// LDS atomics would collide; selected keys are mapped back for their scores.
 template <int NWV, int J>
 __global__ void __launch_bounds__(64 * NWV) topk_reg_kernel(TopkArgs a) {
   constexpr int NT = 64 * NWV;
@@ -276,8 +280,41 @@ __global__ void __launch_bounds__(64 * NWV) topk_reg_kernel(TopkArgs a) {
       for (int e = 0; e < 4; ++e) u[j][e] = i + e < n ? f2key(srow[i + e]) : 0u;
     }
   }
+  // the row's finite key range
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (u[j][e] > KEY_NEG_INF) {
+        kmin = min(kmin, u[j][e]);
+        kmax = max(kmax, u[j][e]);
+      }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) {
+    wtot[wave] = kmin;
+    wtot[NWV + wave] = kmax;
+  }
   for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
   __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    kmin = min(kmin, wtot[w]);
+    kmax = max(kmax, wtot[NWV + w]);
+  }
+  // no finite key: kmin > kmax, nothing is re-based
+  const uint32_t rng = kmax >= kmin ? kmax - kmin : 0u;
+  const int rs = rng ? max(__builtin_clz(rng) - 1, 0) : 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (u[j][e] > KEY_NEG_INF) u[j][e] = KEY_NEG_INF + 1u + ((u[j][e] - kmin) << rs);
+  auto orig_key = [&](uint32_t v) -> uint32_t { return ((v - KEY_NEG_INF - 1u) >> rs) + kmin; };
 #pragma unroll
   for (int j = 0; j < J; ++j)
 #pragma unroll
@@ -409,7 +446,7 @@ __global__ void __launch_bounds__(64 * NWV) topk_reg_kernel(TopkArgs a) {
           else if (bk4) key = bk[j] + i;
           else key = brow[i / a.block_size] * a.block_size + i % a.block_size;
           oidx[pos] = key;
-          if (osc) osc[pos] = key2f(x);
+          if (osc) osc[pos] = key2f(orig_key(x));
         }
         gb += gt ? 1u : 0u;
         eb += eq ? 1u : 0u;
