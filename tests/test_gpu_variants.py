@@ -157,6 +157,18 @@ def test_block_whole_tile_blocks(Bs, keep):
     check_block(p, 256, Bs, keep, gi, gs, gb, [(0, t) for t in range(p.T)], f"block-big-Bs{Bs}")
 
 
+@pytest.mark.parametrize("Bs,keep", [(128, 3), (32, 10)])
+def test_block_ragged_tail_tiles(Bs, keep):
+    # H=64, D=128: a query count that is not a multiple of the refine's work-group, two sequences
+    # with a shorter cache in the second (queries past its end see only the cached keys)
+    p = W.make_prefill(1003, 64, 128, seed=60 + Bs, B=2)
+    p.k_len[1] = 870
+    say(f"case block ragged T=1003 B=2 k_len=(1003, 870) Bs={Bs} keep={keep}")
+    gi, gs, gb = run_block(p, 200, Bs, keep)
+    check_block(p, 200, Bs, keep, gi, gs, gb, [(b, t) for b in range(2) for t in range(p.T)],
+                f"block-ragged-Bs{Bs}")
+
+
 @pytest.mark.parametrize("N,T,Bs,keep", [(40000, 32, 16, 900), (200000, 16, 128, 500)])
 def test_block_union_of_several_rounds(N, T, Bs, keep):
     # uncorrelated queries: the union of a work-group's kept blocks exceeds the 1024 blocks the
