@@ -157,6 +157,14 @@ def test_block_whole_tile_blocks(Bs, keep):
     check_block(p, 256, Bs, keep, gi, gs, gb, [(0, t) for t in range(p.T)], f"block-big-Bs{Bs}")
 
 
+def test_block_whole_tile_blocks_d64():
+    # D=64 and 32 heads through the whole-tile path (Bs=256), partial last block
+    p = W.make_hier(5000, 42, H=32, D=64, seed=45, n_regions=4, region=256)
+    say("case block Bs=256 keep=6 N=5000 T=42 H=32 D=64")
+    gi, gs, gb = run_block(p, 300, 256, 6)
+    check_block(p, 300, 256, 6, gi, gs, gb, [(0, t) for t in range(p.T)], "block-big-d64")
+
+
 @pytest.mark.parametrize("Bs,keep", [(128, 3), (32, 10)])
 def test_block_ragged_tail_tiles(Bs, keep):
     # H=64, D=128: a query count that is not a multiple of the refine's work-group, two sequences
