@@ -322,36 +322,17 @@ __global__ void __launch_bounds__(64 * NWV) topk_reg_kernel(TopkArgs a) {
       if (u[j][e] > KEY_NEG_INF) atomicAdd(&hist[u[j][e] >> 21], 1u);
   __syncthreads();
 
-  // wave 0: total finite count and the bin of the kk-th largest key (32 bins per lane)
-  auto wave_find = [&](int nbins, uint32_t need, bool want_total) {
-    const int per = nbins / 64;
-    const int hi = nbins - 1 - lane * per;
-    uint32_t sum = 0;
-    for (int i = 0; i < per; ++i) sum += hist[hi - i];
-    const uint32_t inc = wave_scan_dpp(sum);
-    const uint32_t tot = wave_bcast(inc, 63);
-    if (want_total) need = min(need, tot);
-    const uint32_t ab = inc - sum;
-    int bin = -1;
-    uint32_t run = ab;
-    if (need > 0 && ab < need && need <= inc) {
-      for (int i = 0; i < per; ++i) {
-        const uint32_t h = hist[hi - i];
-        if (run + h >= need) {
-          bin = hi - i;
-          break;
-        }
-        run += h;
-      }
-    }
-    const uint64_t m = __ballot(bin >= 0);
-    if (lane == 0) bc[2] = tot;
-    if (m) {
-      const int src = __builtin_ctzll(m);
-      const uint32_t rb = wave_bcast((uint32_t)bin, src), ra = wave_bcast(run, src);
-      if (lane == 0) {
-        bc[0] = rb;
-        bc[1] = ra;
+  // wave 0: total finite count and the bin of the need-th largest key, with the bank-spread
+  // histogram walk (a need above the total finds no bin: every finite key is then selected)
+  auto wave_find = [&](int nbins, uint32_t need, bool) {
+    int bin;
+    uint32_t above;
+    const uint32_t tot = wave_hist_find(nbins, need, [&](int i) { return hist[i]; }, &bin, &above);
+    if (lane == 0) {
+      bc[2] = tot;
+      if (bin >= 0) {
+        bc[0] = (uint32_t)bin;
+        bc[1] = above;
       }
     }
   };
