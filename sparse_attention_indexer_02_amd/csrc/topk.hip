@@ -848,7 +848,10 @@ hipError_t launch_topk(const TopkArgs& a, int max_row_len, hipStream_t s) {
   if ((a.score_stride & 3) != 0 || (reinterpret_cast<uintptr_t>(a.scores) & 15) != 0)
     return hipErrorInvalidValue;                 // rows must allow 16-byte loads
   dim3 g(a.n_rows);
-  if (a.row_meta) {
+  // rows of up to 4096 slots: the register selector, even with a summary (paired runs on the
+  // given-set refine's 4096-slot rows: 0.19 against 0.25 ms; at 8192 slots the summary's single
+  // streaming pass is faster, 1.29 against 1.49 ms on the group refine)
+  if (a.row_meta && max_row_len > 4096) {
     const dim3 b(TS_THREADS);
     if (a.k <= TS_OUT) {
       if (a.map_mode == MAP_IDENT) hipLaunchKernelGGL((topk_stream_kernel<MAP_IDENT, false>), g, b, 0, s, a);
