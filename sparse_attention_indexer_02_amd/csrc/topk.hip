@@ -784,14 +784,19 @@ __global__ void __launch_bounds__(256) sort_rows_kernel(int32_t* rows, int strid
 // Ascending order of rows of DISTINCT values in [0, max_value): the values become bits of an LDS
 // bitmap, and each thread writes the set bits of its contiguous range of words at its exclusive
 // prefix of the popcounts. One pass over the row and one over the bitmap.
+// STAGE: the sorted row is assembled in LDS after the bitmap and written out coalesced (each
+// thread's values are contiguous in the output, so direct stores scatter a wave's writes over 64
+// cache lines)
+template <bool STAGE>
 __global__ void __launch_bounds__(256) sort_rows_bitmap_kernel(int32_t* rows, int stride, const int32_t* count,
-                                                               int nwords) {
+                                                               int nwords, int cap) {
   extern __shared__ uint32_t bm[];
+  int32_t* stg = reinterpret_cast<int32_t*>(bm + nwords);   // [cap] when STAGE
   __shared__ uint32_t wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x;
   int32_t* row = rows + (int64_t)r * stride;
-  const int c = count[r];
+  const int c = min(count[r], cap);          // a row holds at most cap values
   for (int i = tid; i < nwords; i += 256) bm[i] = 0u;
   __syncthreads();
   for (int i = tid; i < c; i += 256) {
@@ -808,12 +813,17 @@ __global__ void __launch_bounds__(256) sort_rows_bitmap_kernel(int32_t* rows, in
   __syncthreads();
   uint32_t pos = inc - cnt;
   for (int w = 0; w < wave; ++w) pos += wsum[w];
+  int32_t* dst = STAGE ? stg : row;
   for (int w = w0; w < w1; ++w) {
     uint32_t m = bm[w];
     while (m) {
-      row[pos++] = w * 32 + __builtin_ctz(m);
+      dst[pos++] = w * 32 + __builtin_ctz(m);
       m &= m - 1u;
     }
+  }
+  if constexpr (STAGE) {
+    __syncthreads();
+    for (int i = tid; i < c; i += 256) row[i] = stg[i];
   }
 }
 
@@ -822,13 +832,20 @@ hipError_t launch_sort_rows(int32_t* rows, int stride, const int32_t* count, int
   if (n_rows <= 0 || max_count <= 1) return hipSuccess;
   const int nwords = (max_value + 31) / 32;
   if (max_value > 0 && nwords <= 32768) {
+    const size_t staged = ((size_t)nwords + (size_t)max_count) * sizeof(uint32_t);
+    if (staged <= 65536) {
+      hipLaunchKernelGGL(sort_rows_bitmap_kernel<true>, dim3(n_rows), dim3(256), staged, s, rows, stride, count,
+                         nwords, max_count);
+      return hipGetLastError();
+    }
     const size_t lds = (size_t)nwords * sizeof(uint32_t);
     if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sort_rows_bitmap_kernel),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sort_rows_bitmap_kernel<false>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(sort_rows_bitmap_kernel, dim3(n_rows), dim3(256), lds, s, rows, stride, count, nwords);
+    hipLaunchKernelGGL(sort_rows_bitmap_kernel<false>, dim3(n_rows), dim3(256), lds, s, rows, stride, count, nwords,
+                       max_count);
     return hipGetLastError();
   }
   int pow2 = 1;
