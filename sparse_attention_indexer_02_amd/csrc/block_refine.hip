@@ -3,8 +3,9 @@
 // Efficient Hierarchical Indexing for Fine-Grained Sparse Attention", abstract: the token-level
 // stage runs the original indexer inside the retained candidate blocks).
 //
-// A work-group takes a tile of up to 8 consecutive queries. Adjacent queries keep mostly the same
-// blocks, so the group forms the union of their kept blocks (LDS bitmap + prefix popcounts),
+// A work-group takes a tile of consecutive queries (8, or 4 in the direct bf16 kernel, whose
+// work-groups run two per CU). Adjacent queries keep mostly the same blocks, so the group forms
+// the union of their kept blocks (LDS bitmap + prefix popcounts),
 // streams each union block's keys through LDS once, and every wave runs the MFMA tile only for
 // 32-key steps that hold at least one of its own blocks. Score slot of query t for token
 // o of its p-th kept block = p * block_size + o; tokens past the cache end or past the query's
