@@ -21,6 +21,18 @@ __device__ __forceinline__ void wait_vmem_n() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// ITERS loads of 16 bytes per lane: load i reads base + i STEP into the 1 KB LDS block
+// (i NW + wave) of dst (lane l writing bytes 16 l .. 16 l + 15 of it)
+template <int ITERS, int STEP, int NW>
+__device__ __forceinline__ void load_rows_lds(const uint8_t* base, uint8_t* dst, int wave) {
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i)
+    __builtin_amdgcn_global_load_lds(base + i * STEP,
+                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                         reinterpret_cast<uintptr_t>(dst + (i * NW + wave) * 1024)),
+                                     16, 0, 0);
+}
+
 constexpr int BR_UMAX = 2048;        // union blocks handled per round
 constexpr int BR_NBW = 2048;         // bitmap words: blocks per sequence <= 65536
 constexpr int BRD_UMAX = 1024;       // union blocks per round of the direct kernel
@@ -367,14 +379,33 @@ block_refine_direct_kernel(BlockRefineArgs a) {
         k0_win = j < ntile ? (ublk[v >> lb] << lb) + (v & (Bs - 1)) : 0;
         m_win = (active && j < ntile) ? (int)pos_tab[wave * BRD_UMAX + (v >> lb)] : -1;
       };
+      // A lane's i-th load fills physical chunk p = (i NW + wave) 64 + lane of the tile: row
+      // n_i = i RPI + n_0 and the same logical chunk for every i (the swizzle key repeats every
+      // RPI rows), so its source is the tile's first key row + loff0 + i RPI rows.
+      constexpr int RPI = NW * 64 / G::CPR;               // tile rows per load round
+      static_assert((NW * 64) % G::CPR == 0 && RPI % (1 << G::SWZ_SH) == 0 &&
+                        ((RPI >> G::SWZ_SH) % (G::SWZ + 1)) == 0,
+                    "the swizzle key repeats every load round");
+      const uint32_t loff0 = [&] {
+        const int p0 = wave * 64 + lane;
+        const int n0 = p0 / G::CPR, cp = p0 % G::CPR;
+        return (uint32_t)(n0 * G::ROW_BYTES + ((cp ^ swz<G>(n0)) << 4));
+      }();
       auto load_tile = [&](int j, int k0) {
-        int kx[DLoader::ITERS];
+        uint8_t* dst = tiles + (j % NBUF) * G::TILE_BYTES;
+        if (k0 + KT <= kl) {
+          // every row of the tile is in the cache: one uniform base, no per-row checks
+          const uint8_t* base = kseq + (int64_t)k0 * G::ROW_BYTES + loff0;
+          load_rows_lds<DLoader::ITERS, RPI * G::ROW_BYTES, NW>(base, dst, wave);
+        } else {
+          int kx[DLoader::ITERS];
 #pragma unroll
-        for (int i = 0; i < DLoader::ITERS; ++i) {
-          const int key = k0 + DLoader::row_of(i, wave, lane);
-          kx[i] = key < kl ? key : -1;
+          for (int i = 0; i < DLoader::ITERS; ++i) {
+            const int key = k0 + DLoader::row_of(i, wave, lane);
+            kx[i] = key < kl ? key : -1;
+          }
+          DLoader::load_idx(kseq, dst, wave, lane, kx);
         }
-        DLoader::load_idx(kseq, tiles + (j % NBUF) * G::TILE_BYTES, wave, lane, kx);
       };
       refresh(0);
 #pragma unroll
