@@ -211,10 +211,14 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
 // repeated values are kept once. One work-group per row: the values set bits of an
 // LDS bitmap of N bits, then each thread writes the set bits of its contiguous range of words at
 // the exclusive prefix of the popcounts.
+// STAGE: the ascending set is assembled in LDS after the bitmap ([C] words) and written out
+// coalesced (each thread emits a contiguous run, so direct stores scatter a wave's writes)
+template <bool STAGE>
 __global__ void __launch_bounds__(256) given_lists_kernel(const int32_t* src, const int32_t* cnt, int C,
                                                           int N, const int32_t* k_len, int n_groups,
                                                           int32_t* dst, int32_t* dst_cnt, int nwords) {
   extern __shared__ uint32_t bm[];
+  int32_t* stg = reinterpret_cast<int32_t*>(bm + nwords);
   __shared__ uint32_t wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x;
@@ -238,14 +242,20 @@ __global__ void __launch_bounds__(256) given_lists_kernel(const int32_t* src, co
   __syncthreads();
   uint32_t pos = inc - n;
   for (int w = 0; w < wave; ++w) pos += wsum[w];
+  int32_t* o = STAGE ? stg : out;
   for (int w = w0; w < w1; ++w) {
     uint32_t m = bm[w];
     while (m) {
-      out[pos++] = w * 32 + __builtin_ctz(m);
+      o[pos++] = w * 32 + __builtin_ctz(m);
       m &= m - 1u;
     }
   }
-  if (tid == 0) dst_cnt[r] = (int32_t)(wsum[0] + wsum[1] + wsum[2] + wsum[3]);
+  const int total = (int)(wsum[0] + wsum[1] + wsum[2] + wsum[3]);   // <= c distinct values
+  if constexpr (STAGE) {
+    __syncthreads();
+    for (int i = tid; i < total; i += 256) out[i] = stg[i];
+  }
+  if (tid == 0) dst_cnt[r] = total;
 }
 
 // One wave per member row (b, t) of group g = t / G: the first gcnt[b * NG + g] entries of the
@@ -338,13 +348,19 @@ hipError_t launch_given_lists(const int32_t* src, const int32_t* cnt, int C, int
   if (n_rows <= 0) return hipSuccess;
   const int nwords = (N + 31) / 32;
   if (nwords > 32768) return hipErrorInvalidValue;   // the bitmap must fit in LDS (128 KB)
+  const size_t staged = ((size_t)nwords + (size_t)C) * sizeof(uint32_t);
+  if (staged <= 65536) {
+    hipLaunchKernelGGL(given_lists_kernel<true>, dim3(n_rows), dim3(256), staged, s, src, cnt, C, N, k_len,
+                       n_groups, dst, dst_cnt, nwords);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)nwords * sizeof(uint32_t);
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(given_lists_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(given_lists_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(given_lists_kernel, dim3(n_rows), dim3(256), lds, s, src, cnt, C, N, k_len, n_groups,
+  hipLaunchKernelGGL(given_lists_kernel<false>, dim3(n_rows), dim3(256), lds, s, src, cnt, C, N, k_len, n_groups,
                      dst, dst_cnt, nwords);
   return hipGetLastError();
 }
